@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark one decode step of paged FP8 MLA attention on one MI355X.
+
+A step is the whole hot path on one batch: kv_append_fp8 of the step's new
+latent rows, split-KV mla_decode_paged, and mla_decode_combine.  The default
+workload is one request of 64 heads over a 100,000-token FP8 e4m3 cache
+(+1 appended row) with a per-tensor scale, randomly permuted 64-token pages.
+
+Inputs sit in HBM before timing starts.  Between steps the benchmark rotates
+over several copies of the cache (default 8 x 57.6 MB, more than the 256 MB
+last-level cache) so that every step reads its cache from HBM, as consecutive
+layers of a model would.
+
+Prints one JSON line: the throughput in KV-tokens/s, plus
+* roofline: the decode kernel's algorithmic bytes per launch / its mean
+  duration (HIP events around every launch on its stream) against 8 TB/s;
+* cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "MLA decode KV-tokens/s, HBM TB/s and % roofline, FP8 paged cache @100k ctx"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="fp8_single_100k")
+    ap.add_argument("--rotate", type=int, default=8, help="distinct cache copies cycled over")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-repeats", type=int, default=3)
+    ap.add_argument("--pages-per-split", type=int, default=0)
+    ap.add_argument("--max-splits", type=int, default=0)
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_mla_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"mla_decode_split_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, repeats):
+    """The oracle, as it stands, on the same workload: one full step (append of
+    the new row + attention of every head over the whole context) for request 0."""
+    import numpy as np
+
+    from oracle import mla as omla
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count()
+    b = 0
+    pages = w.pages_of(b)
+    ts = w.tensor_scale() if w.scale_mode == "tensor" else None
+    codes = np.zeros((w.num_pages, 64, 576), np.uint8)
+    scales = np.zeros((w.num_pages, 64), np.float32)
+    c, s = omla.fill_pages_ref(w.page_bits(pages), w.scale_mode, ts)
+    codes[pages], scales[pages] = c, s
+    new = w.new_row_bits()[b:b + 1]
+    q = w.q_bits()[b:b + 1]
+    bt = w.block_table[b:b + 1]
+    sl = w.seq_lens[b:b + 1]
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        omla.append_ref(new, codes, scales, bt, sl, w.scale_mode, ts)
+        omla.decode_ref(q, codes, scales, bt, sl, n_q=w.n_q, H=w.H, cache_dtype=w.cache_dtype,
+                        scale_mode=w.scale_mode, softmax_scale=w.softmax_scale, tensor_scale=ts)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    tokens = int(w.seq_lens[b])
+    return {"value": tokens / t, "unit": "KV-tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"request 0 of {w.name}: append + all {w.H} heads x {tokens} tokens, "
+                      f"median of {repeats} runs of {t:.2f} s (fp64 numpy)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this decode path has "
+              "no multi-GPU mode to benchmark.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import long_context_mla_amd as mla
+    import synth
+
+    dev = torch.device("cuda:0")
+    w = synth.make(args.config)
+    t_setup = time.time()
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q = bf16(w.q_bits())
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    new_rows = bf16(w.new_row_bits()) if w.n_new else None
+    caches, scales = [], []
+    fp8 = w.cache_dtype == "fp8"
+    for r in range(args.rotate):
+        if r == 0:
+            if fp8:
+                cache = torch.zeros((w.num_pages, 64, 576), dtype=torch.uint8, device=dev)
+                if w.scale_mode == "token":
+                    sc = torch.zeros((w.num_pages, 64), dtype=torch.float32, device=dev)
+                else:
+                    sc = torch.tensor([float(w.tensor_scale())], dtype=torch.float32, device=dev)
+                for c0 in range(0, w.num_pages, 4096):
+                    c1 = min(c0 + 4096, w.num_pages)
+                    rows = bf16(w.page_bits(np.arange(c0, c1)).reshape(1, -1, 576))
+                    ident = torch.arange(c0, c1, dtype=torch.int32, device=dev).view(1, -1)
+                    mla.kv_append_fp8(rows, cache, sc, w.scale_mode, ident,
+                                      torch.tensor([(c1 - c0) * 64], dtype=torch.int32, device=dev))
+            else:
+                cache = torch.empty((w.num_pages, 64, 576), dtype=torch.bfloat16, device=dev)
+                for c0 in range(0, w.num_pages, 4096):
+                    c1 = min(c0 + 4096, w.num_pages)
+                    cache[c0:c1] = bf16(w.page_bits(np.arange(c0, c1)))
+                sc = None
+        else:
+            cache = caches[0].clone()
+            sc = None if scales[0] is None else scales[0].clone()
+        caches.append(cache)
+        scales.append(sc)
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+
+    pps = args.pages_per_split or None
+    ms = args.max_splits or None
+    step = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(), dev,
+                          pages_per_split=pps, max_splits=ms)
+    stream = torch.cuda.current_stream()
+
+    def run(i, ev=None):
+        k = i % args.rotate
+        if new_rows is not None:
+            mla.kv_append_fp8(new_rows, caches[k], scales[k], w.scale_mode, bt, sl, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        step.decode(q, caches[k], scales[k], w.scale_mode, bt, sl, w.softmax_scale, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        step.combine(sl, stream=stream)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        run(args.warmup + i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    k_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    k_us = float(k_ms.mean() * 1000)
+
+    tokens = w.total_tokens()
+    unique = w.unique_tokens()
+    kv_bytes = unique * w.kv_row_bytes()
+    fixed_bytes = (w.B * w.n_q * w.H * 576 * 2          # q
+                   + int(sum(-(-int(L) // 64) for L in w.seq_lens)) * 4 + w.B * 4  # page map, lengths
+                   + w.B * w.n_q * w.H * (512 * 2 + 4))  # out + lse
+    alg_bytes = kv_bytes + fixed_bytes
+    flops = 2.0 * w.H * (576 + 512) * sum(
+        sum(int(L) - w.n_q + i + 1 for i in range(w.n_q)) for L in w.seq_lens)
+    achieved_gbs = alg_bytes / (k_us * 1e-6) / 1e9
+    achieved_tflops = flops / (k_us * 1e-6) / 1e12
+    t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    roof = {
+        "bound": bound,
+        "achieved": round(achieved_gbs if bound == "hbm" else achieved_tflops, 1),
+        "peak": HBM_PEAK_GBS if bound == "hbm" else MFMA_BF16_PEAK_TFLOPS,
+        "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+        "frac": round((achieved_gbs / HBM_PEAK_GBS) if bound == "hbm"
+                      else (achieved_tflops / MFMA_BF16_PEAK_TFLOPS), 4),
+        "traffic": load_traffic(w.name),
+        "kernel": "mla_decode_split",
+        "kernel_us": round(k_us, 3),
+        "algorithmic_bytes": int(alg_bytes),
+        "mfma_tflops": round(achieved_tflops, 1),
+    }
+    value = tokens / (ms_step * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.B, "heads": w.H, "queries": w.n_q,
+            "seq_lens_total": tokens, "unique_tokens": unique, "page": 64,
+            "cache": f"{w.cache_dtype}" + (f" ({w.scale_mode} scale)" if fp8 else ""),
+            "rotated_caches": args.rotate, "pages_per_split": step.pps, "max_splits": step.max_splits,
+        },
+        "roofline": roof,
+        "hbm_tb_s_step": round(alg_bytes / (ms_step * 1e-3) / 1e12, 3),
+        "roofline_frac_step": round(max(t_hbm, t_mfma) / (ms_step * 1e-3), 4),
+        "decode_kernel_us_p10_p50_p90": [round(float(np.percentile(k_ms, p)) * 1000, 2) for p in (10, 50, 90)],
+        "setup_s": round(t_setup, 1),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_repeats)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

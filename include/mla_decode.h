@@ -1,0 +1,162 @@
+/*
+ * Paged MLA decode attention over an FP8 (e4m3) or BF16 latent KV cache — C ABI.
+ *
+ * The operation: decode attention for a few new query tokens per request over
+ * a long cache of one shared latent row per token.  The row has 576 elements
+ * (512 latent + 64 rope) and serves as both key and value: models like Kimi
+ * have no distinct keys and values, and the row is 576 elements per token per
+ * layer ("How to serve trillions of tokens for trillion-parameter coding
+ * agents", sections "First, understand the workload" and "Tensor parallel was
+ * the best parallelism strategy for maximum interactivity"); MLA keeps one
+ * latent head shared by all query heads ("vLLM x AgentX: Optimizing for
+ * Real-World Agentic Serving", section "Model-specific parallelism / Kimi K3").
+ * The cache is stored as FP8 e4m3, half the bytes of BF16, and converted as
+ * it is read ("Smaller, faster, safer: running Kimi and GLM at scale", section
+ * "Quantizing the KV cache").  Requests reach physical cache pages through a
+ * per-request page map ("Smaller, faster, safer", section "Protecting a shared
+ * KV cache").  Split-KV partial outputs and their log-sum-exp are merged with
+ * the online-softmax identity ("vLLM x AgentX", section "Model-specific
+ * parallelism / Kimi K3").
+ *
+ * Definitions used by every call:
+ *   D = 576 (row width), DV = 512 (value width = first 512 elements of the row),
+ *   P = 64 tokens per physical page.
+ *   Token t of request b lives in slot t % 64 of physical page
+ *   block_table[b * max_blocks + t / 64].
+ *   seq_lens[b] = L_b counts the tokens request b can see, including rows the
+ *   step has just appended; its n_q queries are positions L_b-n_q .. L_b-1 and
+ *   query i sees tokens t < L_b - n_q + i + 1 (causal among the new tokens).
+ *   Query / output row r = i * H + h.
+ *   E4M3 is the OCP E4M3FN encoding (bias 7, no infinities, max 448).
+ *
+ * Ownership and threading: the caller owns every buffer; the library never
+ * allocates, frees or synchronises.  All pointers except the scalar-out
+ * arguments of mla_decode_plan are device pointers.  Work is enqueued on
+ * `stream` (a hipStream_t; NULL = the default stream) and the calls return
+ * before it runs.  The calls are re-entrant; calls that write the same buffers
+ * must be ordered by the caller.
+ *
+ * Errors: host-detectable argument errors return a non-zero mla_status_t
+ * before anything is launched.  A failed launch returns MLA_ERR_HIP.  No
+ * exception or abort crosses the ABI.  Device-side contents (page ids,
+ * lengths) are not checked on the host: page ids outside [0, num_pages) are
+ * clamped into range and lengths are clamped to [0, max_blocks * 64], so a bad
+ * table gives wrong numbers but never an out-of-bounds access.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_HEAD_DIM 576
+#define MLA_VALUE_DIM 512
+#define MLA_PAGE_SIZE 64
+#define MLA_MAX_HEADS 128
+#define MLA_MAX_QUERIES 8
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL_PTR = 1,
+  MLA_ERR_BAD_SHAPE = 2,
+  MLA_ERR_UNSUPPORTED = 3,
+  MLA_ERR_HIP = 4
+} mla_status_t;
+
+typedef enum { MLA_CACHE_BF16 = 0, MLA_CACHE_FP8_E4M3 = 1 } mla_cache_dtype_t;
+
+typedef enum {
+  MLA_SCALE_NONE = 0,       /* BF16 cache: no scale */
+  MLA_SCALE_PER_TENSOR = 1, /* one fp32 scale for the whole cache: kv_scale[0] */
+  MLA_SCALE_PER_TOKEN = 2   /* one fp32 scale per cached token: kv_scale[page * 64 + slot] */
+} mla_scale_mode_t;
+
+/*
+ * kv_append_fp8 — quantise new latent rows to E4M3 and write them into the
+ * paged cache ("Smaller, faster, safer", section "Quantizing the KV cache":
+ * the cache is stored in FP8 e4m3 instead of BF16).
+ *
+ *   kv_new      bf16 [B, n_new, 576], row-major.  Inputs must be finite.
+ *   kv_cache    e4m3 codes [num_pages, 64, 576] (576 bytes per token row).
+ *   kv_scale    PER_TOKEN: fp32 [num_pages, 64], written for each new row;
+ *               PER_TENSOR: fp32 [1], read.
+ *   block_table int32 [B, max_blocks]; seq_lens int32 [B] (after the append).
+ *
+ * Row j of request b goes to position p = seq_lens[b] - n_new + j.
+ * PER_TOKEN: amax = max_d |x_d|; scale = fp32(amax / 448) (1.0 when amax = 0);
+ * code_d = E4M3(fp32(x_d / scale)).  PER_TENSOR: code_d = E4M3(fp32(x_d / kv_scale[0])).
+ * Divisions are correctly rounded fp32; E4M3() rounds to nearest, ties to the
+ * even code, saturating to +-448.  Positions p < 0 are skipped.
+ * B = 0 or n_new = 0 is a no-op.
+ */
+int kv_append_fp8(const void* kv_new, void* kv_cache, float* kv_scale, int scale_mode,
+                  const int32_t* block_table, const int32_t* seq_lens, int B, int n_new,
+                  int max_blocks, int num_pages, void* stream);
+
+/*
+ * mla_decode_paged — split-KV decode attention over the paged latent cache.
+ *
+ *   q           bf16 [B, n_q, H, 576]: the query already absorbed into the
+ *               latent space (latent 512 | rope 64).
+ *   kv_cache    MLA_CACHE_FP8_E4M3: e4m3 codes [num_pages, 64, 576];
+ *               MLA_CACHE_BF16: bf16 [num_pages, 64, 576].
+ *   kv_scale    see mla_scale_mode_t (NULL allowed for MLA_SCALE_NONE).
+ *   softmax_scale  multiplies q.K before the softmax.
+ *   pages_per_split, max_splits  the split-KV plan (mla_decode_plan gives one):
+ *               split s of request b covers pages [s*pps, (s+1)*pps), except
+ *               that split max_splits-1 also takes every page after it.
+ *   o_partial   fp32 [B, max_splits, n_q, H, 512]: per-split output,
+ *               normalised by the split's own softmax sum.
+ *   lse_partial fp32 [B, max_splits, n_q, H]: per-split natural log-sum-exp
+ *               (-inf for a row that sees no token of the split).
+ *   out         bf16 [B, n_q, H, 512];  lse  fp32 [B, n_q, H] (natural log).
+ *
+ * With max_splits == 1 the final out and lse are written directly and the
+ * partial buffers may be NULL.  With max_splits > 1 only the partials are
+ * written (splits past a request's last page are left untouched) and
+ * mla_decode_combine must run next; out and lse may then be NULL.
+ * Supported: 1 <= H <= 128, 1 <= n_q <= 8.  A row that sees no token gets
+ * out = 0 and lse = -inf.
+ */
+int mla_decode_paged(const void* q, const void* kv_cache, int cache_dtype, const float* kv_scale,
+                     int scale_mode, const int32_t* block_table, const int32_t* seq_lens, int B,
+                     int n_q, int H, int max_blocks, int num_pages, float softmax_scale,
+                     int pages_per_split, int max_splits, float* o_partial, float* lse_partial,
+                     void* out, float* lse, void* stream);
+
+/*
+ * mla_decode_combine — merge the split partials of mla_decode_paged
+ * ("vLLM x AgentX", section "Model-specific parallelism / Kimi K3": partial
+ * outputs and LSE statistics merged with online softmax).
+ *
+ * For each row, over the n_b = min(max_splits, ceil(ceil(L_b/64)/pps)) splits
+ * request b used: M = max_s lse_s; w_s = exp(lse_s - M);
+ * out = bf16(sum_s w_s o_s / sum_s w_s); lse = M + ln(sum_s w_s).
+ * Same shapes as mla_decode_paged; pages_per_split and max_splits must be the
+ * values that call used.
+ */
+int mla_decode_combine(const float* o_partial, const float* lse_partial, const int32_t* seq_lens,
+                       int B, int n_q, int H, int max_blocks, int pages_per_split, int max_splits,
+                       void* out, float* lse, void* stream);
+
+/*
+ * mla_decode_plan — host-only helper that picks pages_per_split and max_splits
+ * so the split workgroups fill `num_cus` compute units (0 = 256) with about
+ * equal work.  max_seq_len and total_seq_len are the largest and the summed
+ * L_b of the batch.  Writes *pages_per_split >= 1 and *max_splits >= 1.
+ * Touches no device.
+ */
+int mla_decode_plan(int B, int n_q, int H, int max_seq_len, int64_t total_seq_len, int num_cus,
+                    int* pages_per_split, int* max_splits);
+
+/* Static text for a status code. */
+const char* mla_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

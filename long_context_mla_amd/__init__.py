@@ -1,0 +1,22 @@
+"""Paged MLA decode attention over an FP8 (e4m3) latent KV cache on MI355X (gfx950).
+
+The compute lives in the HIP library ``libmla_decode.so`` (C ABI in
+``include/mla_decode.h``); this package only binds it.  Importing it without the
+built library raises ImportError: there is no fallback implementation.
+"""
+
+from ._lib import (  # noqa: F401
+    CACHE_BF16,
+    CACHE_FP8_E4M3,
+    LIB_PATH,
+    MlaError,
+    SCALE_NONE,
+    SCALE_PER_TENSOR,
+    SCALE_PER_TOKEN,
+    kv_append_fp8,
+    mla_decode_combine,
+    mla_decode_paged,
+    mla_decode_plan,
+    status_string,
+)
+from .runner import DecodeStep  # noqa: F401

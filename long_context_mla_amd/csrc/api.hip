@@ -1,0 +1,159 @@
+// C-ABI entry points declared in include/mla_decode.h: host-side argument
+// validation (before any HIP call), split planning, and kernel launches on the
+// caller's stream.  No allocation, no synchronisation, no exceptions.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/mla_decode.h"
+#include "device_common.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxGrid = 2147483647;
+
+bool bad_stream_free_shape(int B, int n_q, int H) {
+  return B < 0 || B > 65535 || n_q < 1 || n_q > MLA_MAX_QUERIES || H < 1 || H > MLA_MAX_HEADS;
+}
+
+int check_cache_mode(int cache_dtype, int scale_mode) {
+  if (cache_dtype != MLA_CACHE_BF16 && cache_dtype != MLA_CACHE_FP8_E4M3) return MLA_ERR_UNSUPPORTED;
+  if (scale_mode < MLA_SCALE_NONE || scale_mode > MLA_SCALE_PER_TOKEN) return MLA_ERR_UNSUPPORTED;
+  if (cache_dtype == MLA_CACHE_BF16 && scale_mode != MLA_SCALE_NONE) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL_PTR: return "null pointer argument";
+    case MLA_ERR_BAD_SHAPE: return "bad shape or size argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MLA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int kv_append_fp8(const void* kv_new, void* kv_cache, float* kv_scale, int scale_mode,
+                  const int32_t* block_table, const int32_t* seq_lens, int B, int n_new,
+                  int max_blocks, int num_pages, void* stream) {
+  if (scale_mode != MLA_SCALE_PER_TENSOR && scale_mode != MLA_SCALE_PER_TOKEN) return MLA_ERR_UNSUPPORTED;
+  if (B < 0 || n_new < 0 || max_blocks < 1 || num_pages < 1) return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)B * n_new > kMaxGrid) return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)max_blocks * MLA_PAGE_SIZE > 2147483647LL) return MLA_ERR_BAD_SHAPE;
+  if (B == 0 || n_new == 0) return MLA_OK;
+  if (!kv_new || !kv_cache || !kv_scale || !block_table || !seq_lens) return MLA_ERR_NULL_PTR;
+  mla::AppendArgs a;
+  a.kv_new = static_cast<const uint16_t*>(kv_new);
+  a.cache = static_cast<uint8_t*>(kv_cache);
+  a.kv_scale = kv_scale;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.n_new = n_new;
+  a.max_blocks = max_blocks;
+  a.num_pages = num_pages;
+  const hipError_t e = mla::launch_kv_append(a, scale_mode, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_decode_paged(const void* q, const void* kv_cache, int cache_dtype, const float* kv_scale,
+                     int scale_mode, const int32_t* block_table, const int32_t* seq_lens, int B,
+                     int n_q, int H, int max_blocks, int num_pages, float softmax_scale,
+                     int pages_per_split, int max_splits, float* o_partial, float* lse_partial,
+                     void* out, float* lse, void* stream) {
+  if (int s = check_cache_mode(cache_dtype, scale_mode)) return s;
+  if (bad_stream_free_shape(B, n_q, H)) return MLA_ERR_BAD_SHAPE;
+  if (max_blocks < 1 || num_pages < 1 || pages_per_split < 1 || max_splits < 1) return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)max_blocks * MLA_PAGE_SIZE > 2147483647LL) return MLA_ERR_BAD_SHAPE;
+  if (!std::isfinite(softmax_scale)) return MLA_ERR_BAD_SHAPE;
+  const int R = n_q * H;
+  const int rows = mla::decode_rows_per_group(B, R);
+  const int n_rg = (R + rows - 1) / rows;
+  if ((int64_t)max_splits * n_rg > kMaxGrid) return MLA_ERR_BAD_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!q || !kv_cache || !block_table || !seq_lens) return MLA_ERR_NULL_PTR;
+  if (scale_mode != MLA_SCALE_NONE && !kv_scale) return MLA_ERR_NULL_PTR;
+  if (max_splits == 1 && (!out || !lse)) return MLA_ERR_NULL_PTR;
+  if (max_splits > 1 && (!o_partial || !lse_partial)) return MLA_ERR_NULL_PTR;
+  mla::DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.cache = static_cast<const uint8_t*>(kv_cache);
+  a.kv_scale = kv_scale;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.o_part = o_partial;
+  a.lse_part = lse_partial;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.B = B;
+  a.n_q = n_q;
+  a.H = H;
+  a.R = R;
+  a.max_blocks = max_blocks;
+  a.num_pages = num_pages;
+  a.pps = pages_per_split;
+  a.max_splits = max_splits;
+  a.n_rg = n_rg;
+  a.sm_log2 = softmax_scale * mla::kLog2e;
+  const int kind = cache_dtype == MLA_CACHE_FP8_E4M3 ? mla::kFp8 : mla::kBf16;
+  const hipError_t e = mla::launch_decode(a, kind, scale_mode, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_decode_combine(const float* o_partial, const float* lse_partial, const int32_t* seq_lens,
+                       int B, int n_q, int H, int max_blocks, int pages_per_split, int max_splits,
+                       void* out, float* lse, void* stream) {
+  if (bad_stream_free_shape(B, n_q, H)) return MLA_ERR_BAD_SHAPE;
+  if (max_blocks < 1 || pages_per_split < 1 || max_splits < 1) return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)B * n_q * H * 4 > kMaxGrid) return MLA_ERR_BAD_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!o_partial || !lse_partial || !seq_lens || !out || !lse) return MLA_ERR_NULL_PTR;
+  mla::CombineArgs a;
+  a.o_part = o_partial;
+  a.lse_part = lse_partial;
+  a.seq_lens = seq_lens;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.B = B;
+  a.R = n_q * H;
+  a.max_blocks = max_blocks;
+  a.pps = pages_per_split;
+  a.max_splits = max_splits;
+  const hipError_t e = mla::launch_combine(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_decode_plan(int B, int n_q, int H, int max_seq_len, int64_t total_seq_len, int num_cus,
+                    int* pages_per_split, int* max_splits) {
+  if (!pages_per_split || !max_splits) return MLA_ERR_NULL_PTR;
+  if (bad_stream_free_shape(B, n_q, H) || max_seq_len < 0 || total_seq_len < 0 || num_cus < 0)
+    return MLA_ERR_BAD_SHAPE;
+  if (num_cus == 0) num_cus = 256;
+  const int R = n_q * H;
+  const int rows = mla::decode_rows_per_group(B, R);
+  const int64_t n_rg = (R + rows - 1) / rows;
+  const int64_t max_pages = (max_seq_len + MLA_PAGE_SIZE - 1) / MLA_PAGE_SIZE;
+  // pages of the batch, counting a partial last page per request
+  const int64_t total_pages = (total_seq_len + MLA_PAGE_SIZE - 1) / MLA_PAGE_SIZE + B;
+  if (max_pages == 0) {
+    *pages_per_split = 1;
+    *max_splits = 1;
+    return MLA_OK;
+  }
+  // one workgroup per CU, each with about the same number of pages
+  int64_t pps = (total_pages * n_rg + num_cus - 1) / num_cus;
+  if (pps < 1) pps = 1;
+  if (pps > max_pages) pps = max_pages;
+  int64_t splits = (max_pages + pps - 1) / pps;
+  if (splits * n_rg > kMaxGrid) return MLA_ERR_BAD_SHAPE;
+  *pages_per_split = (int)pps;
+  *max_splits = (int)splits;
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Internal launcher interface between the C-ABI layer (api.hip) and the kernels.
+// Arguments reaching these functions have already been validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct AppendArgs {
+  const uint16_t* kv_new;   // bf16 [B, n_new, 576]
+  uint8_t* cache;           // e4m3 [num_pages, 64, 576]
+  float* kv_scale;          // per token [num_pages, 64] (written) or per tensor [1] (read)
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int B, n_new, max_blocks, num_pages;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;        // bf16 [B, R, 576], R = n_q * H
+  const uint8_t* cache;     // e4m3 or bf16 rows [num_pages, 64, 576]
+  const float* kv_scale;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* o_part;            // fp32 [B, max_splits, R, 512]
+  float* lse_part;          // fp32 [B, max_splits, R]
+  uint16_t* out;            // bf16 [B, R, 512]
+  float* lse;               // fp32 [B, R]
+  int B, n_q, H, R, max_blocks, num_pages, pps, max_splits, n_rg;
+  float sm_log2;            // softmax_scale * log2(e)
+};
+
+struct CombineArgs {
+  const float* o_part;
+  const float* lse_part;
+  const int32_t* seq_lens;
+  uint16_t* out;
+  float* lse;
+  int B, R, max_blocks, pps, max_splits;
+};
+
+// Rows of the query matrix one decode workgroup owns (32 or 64).
+int decode_rows_per_group(int B, int R);
+
+hipError_t launch_kv_append(const AppendArgs& a, int scale_mode, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int cache_kind, int scale_mode, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+}  // namespace mla

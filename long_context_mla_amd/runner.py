@@ -1,0 +1,48 @@
+"""One decode step over a paged latent cache: append the step's new rows (FP8
+cache), split-KV attention, then the split merge — three C-ABI calls on the
+current stream with buffers allocated once per batch shape."""
+
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+
+class DecodeStep:
+    def __init__(self, B, n_q, H, max_blocks, max_seq_len, total_seq_len, device, num_cus=0,
+                 pages_per_split=None, max_splits=None):
+        if pages_per_split is None or max_splits is None:
+            pages_per_split, max_splits = _lib.mla_decode_plan(B, n_q, H, max_seq_len, total_seq_len,
+                                                               num_cus)
+        self.B, self.n_q, self.H, self.max_blocks = B, n_q, H, max_blocks
+        self.pps, self.max_splits = int(pages_per_split), int(max_splits)
+        self.out = torch.empty((B, n_q, H, _lib.VALUE_DIM), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((B, n_q, H), dtype=torch.float32, device=device)
+        if self.max_splits > 1:
+            self.o_partial = torch.empty((B, self.max_splits, n_q, H, _lib.VALUE_DIM),
+                                         dtype=torch.float32, device=device)
+            self.lse_partial = torch.empty((B, self.max_splits, n_q, H), dtype=torch.float32,
+                                           device=device)
+        else:
+            self.o_partial = self.lse_partial = None
+
+    def decode(self, q, kv_cache, kv_scale, scale_mode, block_table, seq_lens, softmax_scale,
+               stream=None):
+        _lib.mla_decode_paged(q, kv_cache, kv_scale, scale_mode, block_table, seq_lens,
+                              softmax_scale, self.pps, self.max_splits, self.o_partial,
+                              self.lse_partial, self.out, self.lse, stream=stream)
+
+    def combine(self, seq_lens, stream=None):
+        if self.max_splits > 1:
+            _lib.mla_decode_combine(self.o_partial, self.lse_partial, seq_lens, self.max_blocks,
+                                    self.pps, self.out, self.lse, stream=stream)
+
+    def __call__(self, q, kv_cache, kv_scale, scale_mode, block_table, seq_lens, softmax_scale,
+                 new_rows=None, stream=None):
+        if new_rows is not None and new_rows.shape[1] > 0:
+            _lib.kv_append_fp8(new_rows, kv_cache, kv_scale, scale_mode, block_table, seq_lens,
+                               stream=stream)
+        self.decode(q, kv_cache, kv_scale, scale_mode, block_table, seq_lens, softmax_scale, stream)
+        self.combine(seq_lens, stream)
+        return self.out, self.lse

@@ -1,0 +1,118 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, rejects bad arguments with status codes before any HIP call, and its
+split planner covers every page.  No kernel runs here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import long_context_mla_amd._lib as L
+
+    return L.LIB
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for fn in ("kv_append_fp8", "mla_decode_paged", "mla_decode_combine"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for fn in _declared():
+        assert hasattr(lib, fn), fn
+    # and through the dynamic symbol table, with C linkage
+    syms = os.popen(f"nm -D --defined-only {lib._name}").read()
+    for fn in _declared():
+        assert re.search(rf"\bT {fn}$", syms, flags=re.M), fn
+
+
+def _decode(lib, **kw):
+    a = dict(q=1, cache=1, dt=1, scale=1, sm=1, bt=1, sl=1, B=1, n_q=1, H=64, mb=10, np_=10,
+             ss=0.07, pps=1, ms=1, op=None, lp=None, out=1, lse=1)
+    a.update(kw)
+    P = lambda v: None if v is None else ctypes.c_void_p(v)  # noqa: E731
+    return lib.mla_decode_paged(P(a["q"]), P(a["cache"]), a["dt"], P(a["scale"]), a["sm"], P(a["bt"]),
+                                P(a["sl"]), a["B"], a["n_q"], a["H"], a["mb"], a["np_"], a["ss"],
+                                a["pps"], a["ms"], P(a["op"]), P(a["lp"]), P(a["out"]), P(a["lse"]), None)
+
+
+def test_decode_argument_validation(lib):
+    # every case fails on the host before a pointer is touched (they are dummies)
+    assert _decode(lib, q=None) == 1
+    assert _decode(lib, scale=None) == 1
+    assert _decode(lib, out=None) == 1
+    assert _decode(lib, ms=4, op=None, lp=None) == 1
+    assert _decode(lib, H=0) == 2
+    assert _decode(lib, H=129) == 2
+    assert _decode(lib, n_q=9) == 2
+    assert _decode(lib, n_q=0) == 2
+    assert _decode(lib, pps=0) == 2
+    assert _decode(lib, ms=0) == 2
+    assert _decode(lib, mb=0) == 2
+    assert _decode(lib, np_=0) == 2
+    assert _decode(lib, B=-1) == 2
+    assert _decode(lib, ss=float("nan")) == 2
+    assert _decode(lib, dt=7) == 3
+    assert _decode(lib, sm=5) == 3
+    assert _decode(lib, dt=0, sm=1) == 3  # bf16 cache takes no scale
+    assert _decode(lib, B=0) == 0  # empty batch: nothing to do
+
+
+def test_append_and_combine_validation(lib):
+    P = ctypes.c_void_p
+    assert lib.kv_append_fp8(P(1), P(1), P(1), 0, P(1), P(1), 1, 1, 1, 1, None) == 3
+    assert lib.kv_append_fp8(None, P(1), P(1), 2, P(1), P(1), 1, 1, 1, 1, None) == 1
+    assert lib.kv_append_fp8(P(1), P(1), P(1), 2, P(1), P(1), -1, 1, 1, 1, None) == 2
+    assert lib.kv_append_fp8(None, None, None, 2, None, None, 0, 4, 1, 1, None) == 0
+    assert lib.mla_decode_combine(None, P(1), P(1), 1, 1, 1, 1, 1, 2, P(1), P(1), None) == 1
+    assert lib.mla_decode_combine(P(1), P(1), P(1), 1, 1, 1, 1, 0, 2, P(1), P(1), None) == 2
+    assert lib.mla_decode_combine(P(1), P(1), P(1), 1, 9, 1, 1, 1, 2, P(1), P(1), None) == 2
+    assert lib.mla_status_string(3) == b"unsupported configuration"
+
+
+@pytest.mark.parametrize("B,n_q,H,maxL,total,cus", [
+    (1, 1, 64, 100_001, 100_001, 256),
+    (32, 1, 64, 137_661, 3_269_170, 256),
+    (64, 1, 64, 74_893, 1_370_066, 256),
+    (16, 4, 64, 142_004, 16 * 142_004, 256),
+    (2, 1, 16, 1000, 1777, 0),
+    (3, 2, 16, 1, 3, 80),
+    (1, 1, 64, 0, 0, 256),
+])
+def test_plan_covers_every_page(B, n_q, H, maxL, total, cus):
+    import long_context_mla_amd as m
+
+    pps, ms = m.mla_decode_plan(B, n_q, H, maxL, total, cus)
+    pages = -(-maxL // 64)
+    assert pps >= 1 and ms >= 1
+    assert pps * ms >= pages
+    assert pps * (ms - 1) < max(pages, 1)  # no split past the longest request
+    if pages:
+        # about one workgroup per CU: rows per group 32 or 64
+        R = n_q * H
+        rows = 32 if (R <= 32 or B * -(-R // 64) < 16) else 64
+        wgs = sum(-(-(-(-L // 64)) // pps) for L in [maxL] * 1) * -(-R // rows)
+        assert wgs >= 1
+
+
+def test_plan_rejects_bad_input():
+    import long_context_mla_amd as m
+
+    with pytest.raises(m.MlaError):
+        m.mla_decode_plan(1, 0, 64, 10, 10)
+    with pytest.raises(m.MlaError):
+        m.mla_decode_plan(1, 1, 64, -1, 10)

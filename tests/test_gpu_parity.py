@@ -1,0 +1,244 @@
+"""GPU parity of the HIP path against the CPU oracle on small workloads that
+span several 64-token tiles, ragged tails, many split plans, every cache and
+scale mode, several query counts and head counts, plus the invariants the
+method has (one visible token, weights summing to one, page permutation,
+determinism, FP8 = BF16 on the e4m3 grid).  All calls go through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import mla as omla
+
+from _gpu import GpuState, compare, log, oracle_decode, oracle_state, bf16_tensor_to_f64
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    dict(name="fp8tok_b3", B=3, n_q=1, H=64, context_lens=(999, 63, 333), cache_dtype="fp8", scale_mode="token"),
+    dict(name="fp8ten_b1", B=1, n_q=1, H=64, context_lens=(5000,), cache_dtype="fp8", scale_mode="tensor"),
+    dict(name="bf16_h16", B=2, n_q=1, H=16, context_lens=(1000, 777), cache_dtype="bf16"),
+    dict(name="fp8_nq2_h16", B=2, n_q=2, H=16, context_lens=(190, 1), cache_dtype="fp8", scale_mode="token"),
+    dict(name="fp8_nq3_h64", B=2, n_q=3, H=64, context_lens=(127, 700), cache_dtype="fp8", scale_mode="token"),
+    dict(name="fp8_nq4_h64", B=2, n_q=4, H=64, context_lens=(1500, 60), cache_dtype="fp8", scale_mode="token"),
+    dict(name="fp8_h40_odd", B=2, n_q=1, H=40, context_lens=(129, 640), cache_dtype="fp8", scale_mode="tensor"),
+    dict(name="bf16_nq4_h16", B=1, n_q=4, H=16, context_lens=(300,), cache_dtype="bf16"),
+    dict(name="fp8_rows64", B=18, n_q=1, H=64, context_lens=tuple(range(40, 40 + 18 * 71, 71)),
+         cache_dtype="fp8", scale_mode="token"),
+    dict(name="bf16_rows64", B=16, n_q=1, H=64, context_lens=tuple(range(64, 64 + 16 * 65, 65)),
+         cache_dtype="bf16"),
+    dict(name="fp8_edges", B=4, n_q=1, H=64, context_lens=(62, 64, 0, 127), cache_dtype="fp8",
+         scale_mode="token"),
+    dict(name="fp8_empty_req", B=2, n_q=1, H=64, context_lens=(0, 100), cache_dtype="fp8",
+         scale_mode="token", append=0),
+]
+
+
+def _make(c, seed=0, **kw):
+    c = dict(c)
+    name = c.pop("name")
+    return synth.custom(name, seed=seed, **c, **kw)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_step_matches_oracle(case):
+    w = _make(case)
+    log(f"case {case['name']} B={w.B} n_q={w.n_q} H={w.H} L={w.seq_lens.tolist()}")
+    g = GpuState(w)
+    ref_o, ref_l = oracle_decode(w)
+    out, lse = g.step()
+    compare(out, lse, ref_o, ref_l, tag=f"{case['name']} planned")
+    # explicit split plans: one split, every page its own split, and a short
+    # max_splits whose last split takes the rest
+    max_pages = int(-(-w.seq_lens.max() // 64))
+    for pps, ms in [(max(max_pages, 1), 1), (1, max(max_pages, 1)), (3, -(-max_pages // 3)), (2, 2)]:
+        o, l = g.decode_only(pps, ms)
+        compare(o, l, ref_o, ref_l, tag=f"{case['name']} pps={pps} splits={ms}")
+
+
+def test_every_split_plan_tiny():
+    w = synth.custom("tiny_all_plans", B=2, n_q=2, H=16, context_lens=(128, 200), cache_dtype="fp8",
+                     scale_mode="token", seed=3)
+    g = GpuState(w)
+    ref_o, ref_l = oracle_decode(w)
+    g.step()  # appends the new rows
+    npg = int(-(-w.seq_lens.max() // 64))
+    for pps in range(1, npg + 1):
+        for ms in sorted({1, 2, -(-npg // pps)}):
+            o, l = g.decode_only(pps, ms)
+            compare(o, l, ref_o, ref_l, tag=f"pps={pps} ms={ms}")
+
+
+def test_named_tiny_bf16_full():
+    w = synth.make("tiny_bf16")
+    g = GpuState(w)
+    ref_o, ref_l = oracle_decode(w)
+    out, lse = g.step()
+    compare(out, lse, ref_o, ref_l, tag="tiny_bf16")
+
+
+def test_append_matches_oracle_bit_exact():
+    import long_context_mla_amd as mla
+
+    for mode in ("token", "tensor"):
+        w = synth.custom(f"append_{mode}", B=5, n_q=3, H=16, context_lens=(0, 61, 64, 1000, 5),
+                         cache_dtype="fp8", scale_mode=mode, seed=21, sigma_kv=3.0)
+        g = GpuState(w)
+        g.step()
+        cache, scales, _ = oracle_state(w)
+        got = g.cache.cpu().numpy()
+        assert np.array_equal(got, cache), f"{mode}: codes differ at {np.argwhere(got != cache)[:5]}"
+        if mode == "token":
+            assert np.array_equal(g.kv_scale.cpu().numpy(), scales)
+    # saturation and an all-zero row, per-tensor scale too small for the data
+    d = torch.device("cuda:0")
+    x = np.zeros((2, 1, 576), np.float32)
+    x[0, 0, :] = np.linspace(-900, 900, 576)
+    bits = synth.bf16_bits(x)
+    cache = torch.zeros((1, 64, 576), dtype=torch.uint8, device=d)
+    bt = torch.zeros((2, 1), dtype=torch.int32, device=d)
+    sl = torch.tensor([1, 2], dtype=torch.int32, device=d)
+    new = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(d)
+    for mode, scale in (("tensor", torch.tensor([1.0], device=d)), ("token", torch.zeros((1, 64), device=d))):
+        cache.zero_()
+        mla.kv_append_fp8(new, cache, scale, mode, bt, sl)
+        torch.cuda.synchronize()
+        ref_c = np.zeros((1, 64, 576), np.uint8)
+        ref_s = np.zeros((1, 64), np.float32)
+        omla.append_ref(bits, ref_c, ref_s, np.zeros((2, 1), np.int32), np.array([1, 2], np.int32), mode,
+                        np.float32(1.0))
+        assert np.array_equal(cache.cpu().numpy(), ref_c), mode
+        if mode == "token":
+            assert np.array_equal(scale.cpu().numpy(), ref_s)
+
+
+def test_one_visible_token_returns_its_value():
+    """L = 1: the only weight is 1, so out is the (dequantised) row itself."""
+    for dtype, mode in (("fp8", "tensor"), ("fp8", "token"), ("bf16", "none")):
+        w = synth.custom("one", B=2, n_q=1, H=64, context_lens=(0, 0), cache_dtype=dtype,
+                         scale_mode=mode, append=1, seed=5)
+        if dtype == "bf16":
+            w = synth.custom("one", B=2, n_q=1, H=64, context_lens=(1, 1), cache_dtype=dtype, seed=5)
+        g = GpuState(w)
+        out, lse = g.step()
+        cache, scales, ts = oracle_state(w)
+        for b in range(w.B):
+            K = omla.request_rows(cache, scales, w.block_table, b, 1, w.cache_dtype, w.scale_mode, ts)
+            want = np.broadcast_to(K[0, :512], (64, 512))
+            assert np.max(np.abs(out[b, 0] - want)) <= np.max(np.abs(want)) * 2.0 ** -8
+            if w.scale_mode != "token":
+                # bf16(v * s) with s = 1 or exactly representable products: exact
+                assert np.array_equal(out[b, 0], np.asarray(
+                    bf16_tensor_to_f64(torch.tensor(want, dtype=torch.float32).to(torch.bfloat16))))
+        ref_o, ref_l = oracle_decode(w)
+        compare(out, lse, ref_o, ref_l, tag=f"one-token {dtype}/{mode}")
+
+
+def test_constant_column_gives_exactly_one():
+    """Value column 0 equal to 1 on every token: out[..., 0] is the sum of the
+    softmax weights, 1 exactly after bf16 rounding."""
+    for dtype in ("fp8", "bf16"):
+        w = synth.custom("ones", B=2, n_q=2, H=64, context_lens=(3000, 70), cache_dtype=dtype,
+                         scale_mode="tensor" if dtype == "fp8" else "none", seed=6)
+        g = GpuState(w)
+        col = g.cache.view(torch.uint8 if dtype == "fp8" else torch.int16)
+        if dtype == "fp8":
+            g.kv_scale.fill_(1.0)
+            col[:, :, 0] = 0x38  # 1.0
+            g.new_rows = None  # keep the cache as written
+        else:
+            col[:, :, 0] = 0x3F80  # 1.0 in bf16
+        o, l = g.decode_only(*_plan(w))
+        assert np.all(o[..., 0] == 1.0), np.unique(o[..., 0])
+
+
+def _plan(w):
+    import long_context_mla_amd as mla
+
+    return mla.mla_decode_plan(w.B, w.n_q, w.H, int(w.seq_lens.max()), w.total_tokens())
+
+
+def test_page_permutation_and_determinism_bitwise():
+    a = synth.custom("perm", B=2, n_q=1, H=64, context_lens=(1111, 400), cache_dtype="fp8",
+                     scale_mode="token", seed=7, permute=False)
+    b = synth.custom("perm", B=2, n_q=1, H=64, context_lens=(1111, 400), cache_dtype="fp8",
+                     scale_mode="token", seed=7, permute=True)
+    # same logical rows: rebuild b's pool so that its physical pages hold a's rows
+    ga = GpuState(a)
+    gb = GpuState(b)
+    for req in range(a.B):
+        pa, pb = a.pages_of(req), b.pages_of(req)
+        gb.cache[torch.from_numpy(pb.astype(np.int64)).cuda()] = ga.cache[torch.from_numpy(pa.astype(np.int64)).cuda()]
+        gb.kv_scale[torch.from_numpy(pb.astype(np.int64)).cuda()] = ga.kv_scale[torch.from_numpy(pa.astype(np.int64)).cuda()]
+    ga.new_rows = gb.new_rows = None
+    plan = _plan(a)
+    oa, la = ga.decode_only(*plan)
+    ob, lb = gb.decode_only(*plan)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+    for _ in range(3):
+        o2, l2 = ga.decode_only(*plan)
+        assert np.array_equal(oa, o2) and np.array_equal(la, l2)
+
+
+def test_fp8_equals_bf16_on_the_e4m3_grid():
+    """Cache values exactly representable in e4m3 with scale 1: the FP8 path and
+    the BF16 path see identical numbers and must agree bit for bit."""
+    w8 = synth.custom("grid", B=2, n_q=2, H=64, context_lens=(900, 130), cache_dtype="fp8",
+                      scale_mode="tensor", seed=8, append=0)
+    g8 = GpuState(w8)
+    g8.kv_scale.fill_(1.0)
+    codes = torch.randint(0, 256, g8.cache.shape, generator=torch.Generator().manual_seed(1),
+                          dtype=torch.int32).to(torch.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38  # no NaN codes
+    g8.cache.copy_(codes.cuda())
+    bf = codes.view(torch.float8_e4m3fn).to(torch.bfloat16)  # exact
+    wb = synth.custom("grid", B=2, n_q=2, H=64, context_lens=(900, 130), cache_dtype="bf16", seed=8)
+    gb = GpuState(wb)
+    gb.cache.copy_(bf.cuda())
+    gb.block_table.copy_(g8.block_table)
+    gb.q.copy_(g8.q)
+    plan = _plan(w8)
+    o8, l8 = g8.decode_only(*plan)
+    ob, lb = gb.decode_only(*plan)
+    assert np.array_equal(o8, ob) and np.array_equal(l8, lb)
+
+
+def test_needles_peaked_softmax():
+    """Keys planted along the query: one token dominates a head, |out| ~ O(1)."""
+    needles = [(0, 777, 3, 0.3), (0, 1500, 17, 0.25), (1, 10, 0, 0.35), (1, 2999, 63, 0.2)]
+    w = synth.custom("needle", B=2, n_q=1, H=64, context_lens=(2000, 3000), cache_dtype="fp8",
+                     scale_mode="token", seed=9, needles=needles)
+    g = GpuState(w)
+    ref_o, ref_l = oracle_decode(w)
+    out, lse = g.step()
+    summ = compare(out, lse, ref_o, ref_l, tag="needles")
+    assert summ["max_ref"] > 0.3
+
+
+def test_combine_matches_oracle_merge():
+    """The merge kernel alone on seeded synthetic partials (some splits empty)."""
+    import long_context_mla_amd as mla
+
+    rng = np.random.default_rng(10)
+    B, n_q, H, max_splits, pps, max_blocks = 3, 2, 16, 6, 2, 12
+    seq = np.array([700, 64, 1], np.int32)  # 11, 1 and 1 pages -> 6, 1, 1 splits
+    o = rng.standard_normal((B, max_splits, n_q, H, 512)).astype(np.float32)
+    ls = rng.uniform(-20, 20, (B, max_splits, n_q, H)).astype(np.float32)
+    ls[0, 2, 0, :5] = -np.inf
+    ls[1, 0, 1, 3] = -np.inf  # a row with no visible token at all
+    d = torch.device("cuda:0")
+    out = torch.empty((B, n_q, H, 512), dtype=torch.bfloat16, device=d)
+    lse = torch.empty((B, n_q, H), dtype=torch.float32, device=d)
+    mla.mla_decode_combine(torch.from_numpy(o).to(d), torch.from_numpy(ls).to(d),
+                           torch.from_numpy(seq).to(d), max_blocks, pps, out, lse)
+    torch.cuda.synchronize()
+    got_o, got_l = bf16_tensor_to_f64(out), lse.cpu().double().numpy()
+    for b in range(B):
+        npg = -(-int(seq[b]) // 64)
+        nb = min(max_splits, -(-npg // pps))
+        ro, rl = omla.merge_ref(o[b, :nb], ls[b, :nb])
+        assert np.max(np.abs(got_o[b] - ro)) <= 2.0 ** -8 * max(1.0, np.abs(ro).max())
+        fin = np.isfinite(rl)
+        assert np.array_equal(fin, np.isfinite(got_l[b]))
+        assert np.max(np.abs(got_l[b][fin] - rl[fin])) <= 1e-5 * 40
