@@ -76,16 +76,78 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Reduction across the four 16-lane groups (lanes l, l^16, l^32, l^48).
+// Reduction across the four 16-lane groups (lanes l, l^16, l^32, l^48), on
+// the VALU: permlane16_swap pairs rows 0/1 and 2/3, permlane32_swap pairs the
+// two halves of the wave.
 __device__ __forceinline__ float group4_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(bits_of(v), bits_of(v), false, false);
+  v = fmaxf(float_of(a[0]), float_of(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(bits_of(v), bits_of(v), false, false);
+  return fmaxf(float_of(b[0]), float_of(b[1]));
 }
 __device__ __forceinline__ float group4_sum(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(bits_of(v), bits_of(v), false, false);
+  v = float_of(a[0]) + float_of(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(bits_of(v), bits_of(v), false, false);
+  return float_of(b[0]) + float_of(b[1]);
+}
+
+// Transposing LDS reads (gfx950).  Within each 16-lane group, lane i of the
+// result holds, for j = 0..7 (b8) or 0..3 (b16), the element at offset
+// (i & 7) (b8) or (i & 3) (b16) of the 8-byte row addressed by lane
+// 2j + (i >> 3) (b8) or 4j + (i >> 2) (b16) of the group.
+__device__ __forceinline__ u32x2 lds_read_tr8(const void* p) {
+  typedef __attribute__((ext_vector_type(2))) int i32x2;
+  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+  typedef __attribute__((ext_vector_type(4))) short i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Hand-placed MFMAs.  The compiler's hazard tracking does not see inside inline
+// asm, so these carry their own wait states: each pair starts with s_nop 2
+// (covers a VALU or v_accvgpr_write producing a source just before), and a
+// result is read by VALU or stored only after mfma_result_fence(), which
+// waits out the MFMA write latency and ties the register so that no reader
+// is scheduled ahead of it.  Back-to-back accumulation into the same
+// registers (SrcC = vDst) needs no wait states.
+//
+// S^T[tok][row] += K[tok][:] . Q[row][:] for two row blocks: K in VGPRs, the
+// two query operands in AGPRs, the accumulators in VGPRs.
+__device__ __forceinline__ void mfma_qk2(f32x4& s0, f32x4& s1, bf16x8 k, bf16x8 q0, bf16x8 q1) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %3, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %2, %4, %1"
+      : "+v"(s0), "+v"(s1)
+      : "v"(k), "a"(q0), "a"(q1));
+}
+// O[row][dim] += P[row][:] . V[:][dim] for two row blocks: P and V in VGPRs,
+// the accumulators in AGPRs.
+__device__ __forceinline__ void mfma_pv2(f32x4& o0, f32x4& o1, bf16x8 p0, bf16x8 p1, bf16x8 v) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %4, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %3, %4, %1"
+      : "+a"(o0), "+a"(o1)
+      : "v"(p0), "v"(p1), "v"(v));
+}
+__device__ __forceinline__ void mfma_result_fence_v(f32x4& r0, f32x4& r1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(r0), "+v"(r1));
+}
+__device__ __forceinline__ void mfma_result_fence_a(f32x4& r) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(r));
+}
+__device__ __forceinline__ void mfma_result_tie_a(f32x4& r) { asm volatile("" : "+a"(r)); }
+// A zero accumulator produced by an MFMA (zero operands, SrcC = 0): it gets
+// the register class of the other MFMA accumulators it merges with, so no
+// copies appear where a zeroed value and an accumulated one meet.
+__device__ __forceinline__ f32x4 mfma_zero() {
+  const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(z, z, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {

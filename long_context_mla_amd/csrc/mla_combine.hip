@@ -3,13 +3,16 @@
 // by peers ("vLLM x AgentX: Optimizing for Real-World Agentic Serving", section
 // "Model-specific parallelism / Kimi K3"), here applied to the splits of one GPU.
 //
-// One workgroup per (request, row, 128-dim chunk): 32 lanes x float4 cover the
-// chunk and 8 groups of 32 lanes stride over the splits; an LDS reduction folds
-// the 8 groups.  Split weights are exp(lse_s - max_s lse_s).
+// One workgroup per (request, row, 128-dim chunk).  The split weights
+// exp(lse_s - max_s lse_s) are computed once, in parallel, into LDS; then 8
+// groups of 32 lanes (one float4 of the chunk per lane) stride over the splits
+// with several loads in flight, and an LDS reduction folds the 8 groups.
 #include "device_common.h"
 #include "launch.h"
 
 namespace mla {
+
+constexpr int kWeightChunk = 1024;  // split weights held in LDS at a time
 
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int chunk = blockIdx.x & 3;
@@ -19,47 +22,67 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int t = threadIdx.x;
   const int c4 = t & 31;  // float4 index inside the 128-dim chunk
   const int g = t >> 5;   // split group
+  __shared__ float s_w[kWeightChunk];
+  __shared__ float s_red[4];
   __shared__ f32x4 s_acc[8][32];
-  __shared__ float s_w[8];
+  __shared__ float s_ws[8];
 
-  int L = min(max(a.seq_lens[b], 0), a.max_blocks * kPage);
+  const int L = min(max(a.seq_lens[b], 0), a.max_blocks * kPage);
   const int n_pages = (L + kPage - 1) / kPage;
   const int n_b = min(a.max_splits, (n_pages + a.pps - 1) / a.pps);
-  const int64_t lse_base = (int64_t)b * a.max_splits * a.R + r;
+  const float* lse_b = a.lse_part + (int64_t)b * a.max_splits * a.R + r;
+  const float* o_b = a.o_part + ((int64_t)b * a.max_splits * a.R + r) * kDV + chunk * 128 + c4 * 4;
+  const int64_t o_stride = (int64_t)a.R * kDV;
 
   float M = -INFINITY;
-  for (int s = 0; s < n_b; ++s) M = fmaxf(M, a.lse_part[lse_base + (int64_t)s * a.R]);
+  for (int s = t; s < n_b; s += 256) M = fmaxf(M, lse_b[(int64_t)s * a.R]);
+  M = wave_max(M);
+  if ((t & 63) == 0) s_red[t >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.0f;
-  if (M != -INFINITY) {
-    for (int s = g; s < n_b; s += 8) {
-      const float ls = a.lse_part[lse_base + (int64_t)s * a.R];
-      if (ls == -INFINITY) continue;
-      const float w = expf(ls - M);
-      const f32x4 o = *reinterpret_cast<const f32x4*>(
-          a.o_part + ((lse_base + (int64_t)s * a.R) * kDV) + chunk * 128 + c4 * 4);
-      acc += w * o;
+  for (int s0 = 0; s0 < n_b; s0 += kWeightChunk) {
+    const int s1 = min(n_b, s0 + kWeightChunk);
+    __syncthreads();
+    for (int s = s0 + t; s < s1; s += 256) {
+      const float ls = lse_b[(int64_t)s * a.R];
+      s_w[s - s0] = (ls == -INFINITY) ? 0.0f : expf(ls - M);
+    }
+    __syncthreads();
+    int s = s0 + g;
+    for (; s + 24 < s1; s += 32) {
+      const f32x4 o0 = *reinterpret_cast<const f32x4*>(o_b + s * o_stride);
+      const f32x4 o1 = *reinterpret_cast<const f32x4*>(o_b + (s + 8) * o_stride);
+      const f32x4 o2 = *reinterpret_cast<const f32x4*>(o_b + (s + 16) * o_stride);
+      const f32x4 o3 = *reinterpret_cast<const f32x4*>(o_b + (s + 24) * o_stride);
+      const float w0 = s_w[s - s0], w1 = s_w[s + 8 - s0], w2 = s_w[s + 16 - s0], w3 = s_w[s + 24 - s0];
+      acc += w0 * o0 + w1 * o1 + w2 * o2 + w3 * o3;
+      wsum += (w0 + w1) + (w2 + w3);
+    }
+    for (; s < s1; s += 8) {
+      const float w = s_w[s - s0];
+      acc += w * *reinterpret_cast<const f32x4*>(o_b + s * o_stride);
       wsum += w;
     }
   }
   s_acc[g][c4] = acc;
-  if (c4 == 0) s_w[g] = wsum;
+  if (c4 == 0) s_ws[g] = wsum;
   __syncthreads();
   if (g == 0) {
     f32x4 tot = s_acc[0][c4];
-    float wt = s_w[0];
+    float wt = s_ws[0];
 #pragma unroll
     for (int k = 1; k < 8; ++k) {
       tot += s_acc[k][c4];
-      wt += s_w[k];
+      wt += s_ws[k];
     }
     const float inv = wt > 0.0f ? 1.0f / wt : 0.0f;
     uint16_t* dst = a.out + (int64_t)br * kDV + chunk * 128 + c4 * 4;
     const uint32_t lo = float_to_bf16(tot[0] * inv) | (uint32_t(float_to_bf16(tot[1] * inv)) << 16);
     const uint32_t hi = float_to_bf16(tot[2] * inv) | (uint32_t(float_to_bf16(tot[3] * inv)) << 16);
-    u32x2 v = {lo, hi};
-    *reinterpret_cast<u32x2*>(dst) = v;
+    *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
     if (chunk == 0 && c4 == 0) a.lse[br] = wt > 0.0f ? M + logf(wt) : -INFINITY;
   }
 }

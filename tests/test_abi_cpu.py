@@ -102,11 +102,10 @@ def test_plan_covers_every_page(B, n_q, H, maxL, total, cus):
     assert pps * ms >= pages
     assert pps * (ms - 1) < max(pages, 1)  # no split past the longest request
     if pages:
-        # about one workgroup per CU: rows per group 32 or 64
-        R = n_q * H
-        rows = 32 if (R <= 32 or B * -(-R // 64) < 16) else 64
-        wgs = sum(-(-(-(-L // 64)) // pps) for L in [maxL] * 1) * -(-R // rows)
-        assert wgs >= 1
+        # about one workgroup (32 query rows, pages_per_split pages) per CU
+        rows_groups = -(-(n_q * H) // 32)
+        total_pages = -(-total // 64) + B
+        assert pps <= max(1, -(-(total_pages * rows_groups) // (cus or 256)))
 
 
 def test_plan_rejects_bad_input():
