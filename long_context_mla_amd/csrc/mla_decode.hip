@@ -265,11 +265,18 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < KB / 2; ++i) kraw[i] = *reinterpret_cast<const u32x4*>(kbase + 64 * i);
         __builtin_amdgcn_sched_barrier(0);  // reads ahead of the math
+        // convert three k-blocks into distinct registers, then issue their six
+        // MFMAs: consecutive MFMAs never wait on a register still being read
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const u32x4 w = kraw[kb >> 1];
-          const bf16x8 kop = e4m3x8_to_bf16x8((kb & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]});
-          mfma_qk2(S[0], S[1], kop, qop[0][kb], qop[1][kb]);
+        for (int k0 = 0; k0 < KB; k0 += 3) {
+          bf16x8 kop[3];
+#pragma unroll
+          for (int k = 0; k < 3; ++k) {
+            const u32x4 w = kraw[(k0 + k) >> 1];
+            kop[k] = e4m3x8_to_bf16x8(((k0 + k) & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]});
+          }
+#pragma unroll
+          for (int k = 0; k < 3; ++k) mfma_qk2(S[0], S[1], kop[k], qop[0][k0 + k], qop[1][k0 + k]);
         }
       } else {
 #pragma unroll
@@ -403,17 +410,24 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
           }
         }
         __builtin_amdgcn_sched_barrier(0);  // reads ahead of the math
+        // convert two V blocks into distinct registers, then issue their four MFMAs
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          bf16x8 vop;
-          if constexpr (CACHE == kFp8)
-            vop = e4m3x8_to_bf16x8(vraw[db][0]);
-          else
-            vop = __builtin_bit_cast(bf16x8, u32x4{vraw[db][0].x, vraw[db][0].y,
-                                                   vraw[db][CACHE == kFp8 ? 0 : 1].x,
-                                                   vraw[db][CACHE == kFp8 ? 0 : 1].y});
+        for (int d0 = 0; d0 < 8; d0 += 2) {
+          bf16x8 vop[2];
 #pragma unroll
-          for (int rbp = 0; rbp < 2; ++rbp) O[rbp][db] = mfma_16x16x32_bf16(pop[rbp], vop, O[rbp][db]);
+          for (int d = 0; d < 2; ++d) {
+            if constexpr (CACHE == kFp8)
+              vop[d] = e4m3x8_to_bf16x8(vraw[d0 + d][0]);
+            else
+              vop[d] = __builtin_bit_cast(bf16x8, u32x4{vraw[d0 + d][0].x, vraw[d0 + d][0].y,
+                                                        vraw[d0 + d][CACHE == kFp8 ? 0 : 1].x,
+                                                        vraw[d0 + d][CACHE == kFp8 ? 0 : 1].y});
+          }
+#pragma unroll
+          for (int d = 0; d < 2; ++d)
+#pragma unroll
+            for (int rbp = 0; rbp < 2; ++rbp)
+              O[rbp][d0 + d] = mfma_16x16x32_bf16(pop[rbp], vop[d], O[rbp][d0 + d]);
         }
       }
     }
