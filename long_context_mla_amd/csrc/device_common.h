@@ -35,6 +35,16 @@ __device__ __forceinline__ float bf16_to_float(uint16_t b) { return float_of(uin
 __device__ __forceinline__ uint16_t float_to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
+// Two floats -> two bf16 in one dword (lo = a), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// acc + lo + hi of a dword holding two bf16 values, in fp32.
+__device__ __forceinline__ float dot2_bf16_ones(uint32_t pk, float acc) {
+  const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
+}
 
 // Four E4M3 bytes -> four bf16 values (exact: every E4M3 value is a bf16 value).
 __device__ __forceinline__ void e4m3x4_to_bf16(uint32_t w, bf16x2& lo, bf16x2& hi) {
@@ -135,6 +145,15 @@ __device__ __forceinline__ void mfma_pv2(f32x4& o0, f32x4& o1, bf16x8 p0, bf16x8
       : "+a"(o0), "+a"(o1)
       : "v"(p0), "v"(p1), "v"(v));
 }
+// The same for the first k-block: accumulators start from the inline constant 0.
+__device__ __forceinline__ void mfma_qk2_first(f32x4& s0, f32x4& s1, bf16x8 k, bf16x8 q0, bf16x8 q1) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %2, %3, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %2, %4, 0"
+      : "=&v"(s0), "=&v"(s1)
+      : "v"(k), "a"(q0), "a"(q1));
+}
 __device__ __forceinline__ void mfma_result_fence_v(f32x4& r0, f32x4& r1) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(r0), "+v"(r1));
 }
@@ -142,6 +161,15 @@ __device__ __forceinline__ void mfma_result_fence_a(f32x4& r) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(r));
 }
 __device__ __forceinline__ void mfma_result_tie_a(f32x4& r) { asm volatile("" : "+a"(r)); }
+// A value placed in AGPRs (a copy, once); later "a"-constrained uses keep it there.
+__device__ __forceinline__ bf16x8 to_agpr(bf16x8 v) {
+  bf16x8 r;
+  asm volatile("" : "=a"(r) : "0"(v));
+  return r;
+}
+// Orders readers of MFMA results after this point without waiting: for use
+// where enough other instructions already separate them from the MFMAs.
+__device__ __forceinline__ void mfma_result_tie_v(f32x4& r0, f32x4& r1) { asm volatile("" : "+v"(r0), "+v"(r1)); }
 // A zero accumulator produced by an MFMA (zero operands, SrcC = 0): it gets
 // the register class of the other MFMA accumulators it merges with, so no
 // copies appear where a zeroed value and an accumulated one meet.

@@ -48,8 +48,15 @@ struct Tile {
   static constexpr int ELEM = CACHE == kFp8 ? 1 : 2;
   static constexpr int ROW_BYTES = kD * ELEM;
   static constexpr int PAGE_BYTES = kPage * ROW_BYTES;
-  static constexpr int NBUF = CACHE == kFp8 ? 3 : 2;
+  // FP8 pages are small enough for four LDS buffers, which lets P V of a page
+  // run one iteration after its scores (one barrier per page) with two pages
+  // in flight.  BF16 pages fit twice: scores and P V of a page in the same
+  // iteration, one page in flight.
+  static constexpr bool PIPE = CACHE == kFp8;
+  static constexpr int NBUF = PIPE ? 4 : 2;
+  static constexpr int DIST = PIPE ? 2 : 1;          // pages in flight ahead of the current one
   static constexpr int LOADS = PAGE_BYTES / 4096;  // 16-byte LDS-DMA loads per wave per page
+  static constexpr int PART = LOADS / 3;           // loads issued at each of three points
   static constexpr int PSTRIDE = kPage * 2 + 16;   // bytes per P row in LDS
   static constexpr int KBATCH = 9;                 // BF16 K reads issued before their math
 };
@@ -83,16 +90,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// HBM -> LDS copy without VGPRs: each lane moves 16 (or 4) bytes from its own
-// global address to lds_base + lane * 16 (or 4).  Issued through inline asm so
-// the compiler does not serialise later LDS reads on it; completion is awaited
-// explicitly with wait_vmcnt() followed by a barrier.
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(lds_base) : "memory", "m0");
+// HBM -> LDS copy without VGPRs: each lane moves 16 (or 4) bytes from
+// base + its own 32-bit offset to lds_base + lane * 16 (or 4); the base is a
+// wave-uniform 64-bit address in SGPRs, so a page costs no vector ALU work.
+// Issued through inline asm so the compiler does not serialise later LDS reads
+// on it; completion is awaited explicitly with wait_vmcnt() and a barrier.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(lds_base) : "memory", "m0");
 }
-__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+__device__ __forceinline__ void lds_dma4(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(off), "s"(base), "s"(lds_base) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma16_lane(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(g), "s"(lds_base) : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -113,12 +125,12 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
   using Z = Swz<CACHE>;
   __shared__ __attribute__((aligned(16))) uint8_t s_kv[T::NBUF][T::PAGE_BYTES];
   __shared__ __attribute__((aligned(16))) float s_scale[T::NBUF][kPage];
-  __shared__ __attribute__((aligned(16))) uint8_t s_p[kRows * T::PSTRIDE];
-  __shared__ float s_max[4][kRows];
+  __shared__ __attribute__((aligned(16))) uint8_t s_p[2][kRows * T::PSTRIDE];
+  __shared__ float s_red[4][kRows];   // per-wave row maxima (first page, restarts)
   __shared__ float s_lsum[4][kRows];
   __shared__ float s_lnrm[4][kRows];
   __shared__ float s_m0[kRows];
-  __shared__ int s_flag[4];
+  __shared__ __attribute__((aligned(16))) int s_flag[2][4];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -159,31 +171,26 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
     return;
   }
   const int p_end = split == a.max_splits - 1 ? n_pages : min(n_pages, p_begin + a.pps);
+  const int n_it = p_end - p_begin;
   const float tscale = SCALE == kScaleTensor ? load_const(a.kv_scale, 0) : 1.0f;
   const float coef = a.sm_log2 * tscale;
 
-  // ---- query operands of this lane's rows rb*16 + m (rb = 0, 1), and the
-  // causal limit of each: row i*H + h sees tokens t < L - n_q + i + 1
-  bf16x8 qop[2][kD / 32];
-  int lim[2];
+  // ---- the query of the group's 32 rows, HBM -> LDS in one coalesced copy
+  // shared by the four waves, into the page buffer that stays free until the
+  // second page copy.  Row r's 16-byte chunk c (72 per row) goes to slot
+  // r * 72 + (c ^ ((r / 2) % 8)), which makes the operand reads below free of
+  // bank conflicts.  Rows past R repeat row R - 1 (their results are dropped).
+  constexpr int QBUF = T::NBUF - 1;
+  const uint32_t qlds = lds_addr(&s_kv[QBUF][0]);
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int row = r0 + rb * 16 + m;
-    lim[rb] = row < a.R ? L - a.n_q + row / a.H + 1 : 0;
-    const uint16_t* qrow = a.q + ((int64_t)b * a.R + min(row, a.R - 1)) * kD;
-#pragma unroll
-    for (int kb = 0; kb < kD / 32; ++kb) {
-      // the dims of this lane's 8 slots of k-block kb: k-blocks are paired so
-      // that a lane's slots of k-blocks 2i and 2i+1 are 16 consecutive dims
-      // (one 16-byte FP8 chunk of K); both cache types use this order
-      const int d0 = 64 * (kb >> 1) + 16 * g + 8 * (kb & 1);
-      u32x4 w = *reinterpret_cast<const u32x4*>(qrow + d0);
-      if (row >= a.R) w = u32x4{0u, 0u, 0u, 0u};
-      qop[rb][kb] = __builtin_bit_cast(bf16x8, w);
-    }
+  for (int j = 0; j < 9; ++j) {
+    const int slot = (wave * 9 + j) * 64 + lane;  // 2304 slots = 32 rows x 72 chunks
+    const int r = slot / 72;
+    const int c = (slot - r * 72) ^ ((r >> 1) & 7);
+    const uint16_t* src = a.q + ((int64_t)b * a.R + min(r0 + r, a.R - 1)) * kD + c * 8;
+    lds_dma16_lane(src, qlds + (wave * 9 + j) * 1024);
   }
 
-  constexpr int LPP = T::LOADS + (SCALE == kScaleToken ? 1 : 0);  // loads per page per wave
   // Page ids of the split, 64 at a time, one per lane; picked out with readlane
   // so the DMA issue never waits on a scalar load.
   const int64_t bt_row = (int64_t)b * a.max_blocks;
@@ -194,7 +201,21 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
   };
   int id_chunk = 0;
   int ids = load_ids(p_begin);
-  // each lane's source offsets inside a page for its LOADS LDS chunk slots
+
+  // causal limit of this lane's rows rb*16 + m: row i*H + h sees tokens
+  // t < L - n_q + i + 1; lim_lo is the first token any real row of the group
+  // masks, so earlier pages need no mask (rows past R only pad the group)
+  int lim[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = r0 + rb * 16 + m;
+    lim[rb] = row < a.R ? L - a.n_q + row / a.H + 1 : 0;
+  }
+  const int lim_lo = L - a.n_q + r0 / a.H + 1;
+
+  constexpr int LPP = T::LOADS + (SCALE == kScaleToken ? 1 : 0);  // loads per page per wave
+  // each lane's source offsets inside a page for its LOADS LDS chunk slots;
+  // wave w copies tokens 16w .. 16w+15, the rows its own QK^T reads
   uint32_t goff[T::LOADS];
 #pragma unroll
   for (int j = 0; j < T::LOADS; ++j) {
@@ -202,27 +223,63 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
     const int t = slot / Z::NCH;
     goff[j] = t * T::ROW_BYTES + Z::chunk_of_slot(t, slot - t * Z::NCH) * 16;
   }
-  auto issue = [&](int p, int buf) {
-    const int rel = p - p_begin;
-    if ((rel >> 6) != id_chunk) {
-      id_chunk = rel >> 6;
+  // the page a DMA batch copies: uniform source base and LDS destination
+  const uint8_t* dma_src = a.cache;
+  uint32_t dma_dst = 0;
+  auto dma_page = [&](int it) {  // select page p_begin + it for the following dma_part calls
+    if ((it >> 6) != id_chunk) {
+      id_chunk = it >> 6;
       ids = load_ids(p_begin + (id_chunk << 6));
     }
-    const int pg = __builtin_amdgcn_readlane(ids, rel & 63);
-    const uint8_t* src = a.cache + (int64_t)pg * T::PAGE_BYTES;
-    const uint32_t dst = lds_addr(&s_kv[buf][0]) + wave * T::LOADS * 1024;
+    const int pg = __builtin_amdgcn_readlane(ids, it & 63);
+    dma_src = a.cache + (int64_t)pg * T::PAGE_BYTES;
+    dma_dst = lds_addr(&s_kv[it % T::NBUF][0]) + wave * T::LOADS * 1024;
+    if (SCALE == kScaleToken)
+      lds_dma4(a.kv_scale + (int64_t)pg * kPage, lane * 4, lds_addr(&s_scale[it % T::NBUF][0]));
+  };
+  auto dma_part = [&](int part) {
 #pragma unroll
-    for (int j = 0; j < T::LOADS; ++j) lds_dma16(src + goff[j], dst + j * 1024);
-    if (SCALE == kScaleToken) lds_dma4(a.kv_scale + (int64_t)pg * kPage + lane, lds_addr(&s_scale[buf][0]));
+    for (int j = 0; j < T::LOADS; ++j)
+      if (j / T::PART == part || (part == 2 && j >= 3 * T::PART))
+        lds_dma16(dma_src, goff[j], dma_dst + j * 1024);
   };
   auto prologue = [&]() {
 #pragma unroll
-    for (int k = 0; k < T::NBUF - 1; ++k)
-      if (p_begin + k < p_end) issue(p_begin + k, k);
+    for (int k = 0; k < T::DIST; ++k)
+      if (k < n_it) {
+        dma_page(k);
+        dma_part(0);
+        dma_part(1);
+        dma_part(2);
+      }
   };
   prologue();
 
+  // ---- query operands LDS -> AGPRs: lane (m, g) holds rows rb*16 + m, and
+  // for k-block kb the 8 dims 64(kb/2) + 16g + 8(kb%2) .. +8: k-blocks are
+  // paired so that a lane's slots of k-blocks 2i and 2i+1 are the 16
+  // consecutive dims of one 16-byte FP8 chunk of K (both cache types use
+  // this order).  The wait covers the query only, not the pages behind it.
+  if (T::DIST == 2 && n_it >= 2)
+    wait_vmcnt<2 * LPP>();
+  else
+    wait_vmcnt<LPP>();
+  __syncthreads();
+  bf16x8 qop[2][kD / 32];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = rb * 16 + m;
+#pragma unroll
+    for (int kb = 0; kb < kD / 32; ++kb) {
+      const int c = 8 * (kb >> 1) + 2 * g + (kb & 1);
+      qop[rb][kb] = to_agpr(*reinterpret_cast<const bf16x8*>(
+          &s_kv[QBUF][(row * 72 + (c ^ ((row >> 1) & 7))) * 16]));
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the query buffer is free to be overwritten
+
   float m0[2] = {-INFINITY, -INFINITY};  // log2-domain reference of this lane's rows
+  float ymax[2] = {-INFINITY, -INFINITY}; // running max of score - reference, this lane's tokens
   float lsum[2] = {0.0f, 0.0f};          // this lane's share of the softmax sums (fp32 P)
   float lnrm[2] = {0.0f, 0.0f};          // the same over the bf16-rounded P that PV uses
   f32x4 O[2][8];                          // rows rb*16 + 4g + i, dims 128*wave + 16db + m
@@ -233,203 +290,327 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
   bool have_ref = false;
   int restarts = 0;
 
-  for (int p = p_begin, it = 0; p < p_end; ++p, ++it) {
-    const int buf = it % T::NBUF;
-    if (p + T::NBUF - 2 < p_end)
-      wait_vmcnt<(T::NBUF - 2) * LPP>();
-    else
-      wait_vmcnt<0>();
-    __syncthreads();  // page p is in LDS; every wave is done with page p-1
-    if (p + T::NBUF - 1 < p_end) issue(p + T::NBUF - 1, (it + T::NBUF - 1) % T::NBUF);
-    uint8_t* kv = s_kv[buf];
-    const int tbase = p * kPage;
-    const int nvalid = min(kPage, L - tbase);
-    if (nvalid < kPage) {
-      // rows past the end of the request may hold anything (even NaN codes):
-      // zero them so that their zero weights give zero products in PV
-      u32x4* junk = reinterpret_cast<u32x4*>(kv + nvalid * T::ROW_BYTES);
-      for (int e = threadIdx.x; e < (kPage - nvalid) * (T::ROW_BYTES / 16); e += 256)
-        junk[e] = u32x4{0u, 0u, 0u, 0u};
-    }
+  // per-lane LDS offsets of the PV operand reads (FP8): lane 2j+h of a 16-lane
+  // group addresses token 8g+j (+32 kt) of its wave's dims; the chunk slot of
+  // dims 128w + 64(db/4) + 16(db%4) is 8w + 4(db/4) + ((db%4) ^ f), f = (token/4)%4
+  uint32_t voff[4];
+  {
+    const int t = g * 8 + (m >> 1);
+    const int f = (t >> 2) & 3;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb)
+      voff[bb] = (uint32_t)((t * Z::NCH + wave * 8 + (bb ^ f)) * 16 + 8 * (m & 1));
+  }
+  const int tok = wave * 16 + m;  // this lane's token in QK^T
+  const uint32_t klane = (uint32_t)((tok * Z::NCH + Z::slot(tok, g)) * 16);  // FP8 K chunk base
 
-    // ---- S^T[token][row] = K Q^T for tokens 16*wave .. +16 of the page
-    f32x4 S[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    {
-      constexpr int KB = kD / 32;
-      const int tok = wave * 16 + m;
-      if constexpr (CACHE == kFp8) {
-        // chunk 4i + g of token tok sits at slot 4i + (g ^ f): a fixed per-lane
-        // base plus 64 i; each 16-byte read feeds k-blocks 2i and 2i+1
-        const uint8_t* kbase = kv + (tok * Z::NCH + Z::slot(tok, g)) * 16;
-        u32x4 kraw[KB / 2];
+  // ---- P V over this wave's 128 dims for the page in buffer kvp, with its
+  // weights in P buffer pp; mid() runs between the two 32-token halves
+  auto pv = [&](const uint8_t* kvp, const uint8_t* pp, auto mid) {
+    const int dim0 = wave * 128;
 #pragma unroll
-        for (int i = 0; i < KB / 2; ++i) kraw[i] = *reinterpret_cast<const u32x4*>(kbase + 64 * i);
-        __builtin_amdgcn_sched_barrier(0);  // reads ahead of the math
-        // convert three k-blocks into distinct registers, then issue their six
-        // MFMAs: consecutive MFMAs never wait on a register still being read
+    for (int kt = 0; kt < 2; ++kt) {
+      if (kt == 1) mid();
+      // P (rows x 32 tokens) and V operands of this half of the page are read
+      // first, then converted and fed to the MFMAs; the lane's 8 contraction
+      // slots are tokens tok0 .. tok0+7 in both
+      const int tok0 = kt * 32 + g * 8;
+      bf16x8 pop[2];
+      u32x2 vraw[8][CACHE == kFp8 ? 1 : 2];
 #pragma unroll
-        for (int k0 = 0; k0 < KB; k0 += 3) {
-          bf16x8 kop[3];
+      for (int rbp = 0; rbp < 2; ++rbp)
+        pop[rbp] = *reinterpret_cast<const bf16x8*>(pp + (rbp * 16 + m) * T::PSTRIDE + tok0 * 2);
 #pragma unroll
-          for (int k = 0; k < 3; ++k) {
-            const u32x4 w = kraw[(k0 + k) >> 1];
-            kop[k] = e4m3x8_to_bf16x8(((k0 + k) & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]});
-          }
-#pragma unroll
-          for (int k = 0; k < 3; ++k) mfma_qk2(S[0], S[1], kop[k], qop[0][k0 + k], qop[1][k0 + k]);
+      for (int db = 0; db < 8; ++db) {
+        if constexpr (CACHE == kFp8) {
+          vraw[db][0] = lds_read_tr8(kvp + voff[db & 3] + kt * 32 * T::ROW_BYTES + 64 * (db >> 2));
+        } else {
+          // lane 4j+q of the group addresses token tok0+j (+4), elements dcol+4q .. +4
+          const int dcol = dim0 + db * 16;
+          const int c = (dcol >> 3) + ((m & 3) >> 1);
+          const int t0 = tok0 + (m >> 2), t1 = t0 + 4;
+          vraw[db][0] = lds_read_tr16(kvp + (t0 * Z::NCH + Z::slot(t0, c)) * 16 + 8 * (m & 1));
+          vraw[db][CACHE == kFp8 ? 0 : 1] = lds_read_tr16(kvp + (t1 * Z::NCH + Z::slot(t1, c)) * 16 + 8 * (m & 1));
         }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // reads ahead of the math
+      // convert two V blocks into distinct registers, then issue their four MFMAs
+#pragma unroll
+      for (int d0 = 0; d0 < 8; d0 += 2) {
+        bf16x8 vop[2];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          if constexpr (CACHE == kFp8)
+            vop[d] = e4m3x8_to_bf16x8(vraw[d0 + d][0]);
+          else
+            vop[d] = __builtin_bit_cast(bf16x8, u32x4{vraw[d0 + d][0].x, vraw[d0 + d][0].y,
+                                                      vraw[d0 + d][CACHE == kFp8 ? 0 : 1].x,
+                                                      vraw[d0 + d][CACHE == kFp8 ? 0 : 1].y});
+        }
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+          for (int rbp = 0; rbp < 2; ++rbp)
+            O[rbp][d0 + d] = mfma_16x16x32_bf16(pop[rbp], vop[d], O[rbp][d0 + d]);
+      }
+    }
+  };
+  auto no_mid = [] {};
+
+  // ---- S^T[token][row] = K Q^T for this wave's 16 tokens of the page, all
+  // 32 rows: from the FP8 bytes already read (kraw) or, BF16, from LDS
+  constexpr int KB = kD / 32;
+  u32x4 kraw[KB / 2];
+  auto qk_fp8 = [&](f32x4 (&S)[2]) {
+    // convert three k-blocks into distinct registers, then issue their six
+    // MFMAs: consecutive MFMAs never wait on a register still being read
+#pragma unroll
+    for (int k0 = 0; k0 < KB; k0 += 3) {
+      bf16x8 kop[3];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const u32x4 w = kraw[(k0 + k) >> 1];
+        kop[k] = e4m3x8_to_bf16x8(((k0 + k) & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]});
+      }
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        if (k0 + k == 0)
+          mfma_qk2_first(S[0], S[1], kop[k], qop[0][0], qop[1][0]);
+        else
+          mfma_qk2(S[0], S[1], kop[k], qop[0][k0 + k], qop[1][k0 + k]);
+      }
+    }
+  };
+  auto qk_bf16 = [&](const uint8_t* kv, f32x4 (&S)[2]) {
+#pragma unroll
+    for (int k0 = 0; k0 < KB; k0 += T::KBATCH) {
+      u32x4 kr[T::KBATCH];
+#pragma unroll
+      for (int k = 0; k < T::KBATCH; ++k) {
+        const int kb = k0 + k;
+        const int c = 8 * (kb >> 1) + 2 * g + (kb & 1);  // dims 64(kb/2) + 16g + 8(kb&1) .. +8
+        kr[k] = *reinterpret_cast<const u32x4*>(kv + (tok * Z::NCH + Z::slot(tok, c)) * 16);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // reads ahead of the math
+#pragma unroll
+      for (int k = 0; k < T::KBATCH; ++k) {
+        const bf16x8 kop = __builtin_bit_cast(bf16x8, kr[k]);
+        if (k0 + k == 0)
+          mfma_qk2_first(S[0], S[1], kop, qop[0][0], qop[1][0]);
+        else
+          mfma_qk2(S[0], S[1], kop, qop[0][k0 + k], qop[1][k0 + k]);
+      }
+    }
+  };
+
+  // ---- softmax, part 1: y = score * coef - reference (log2 units), masked
+  // past each row's causal limit, and the running maxima.  Lane holds tokens
+  // 16w + 4g + i of rows rb*16 + m.
+  float y[2][4];
+  f32x4 sc = {1.0f, 1.0f, 1.0f, 1.0f};
+  auto scores = [&](const f32x4 (&S)[2], int it) {
+    const int buf = it % T::NBUF;
+    const int tbase = (p_begin + it) * kPage;
+    float cs[4];
+    if (SCALE == kScaleToken) {
+      sc = *reinterpret_cast<const f32x4*>(&s_scale[buf][wave * 16 + 4 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cs[i] = coef * sc[i];
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float mr = m0[rb] == -INFINITY ? 0.0f : m0[rb];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        y[rb][i] = __builtin_fmaf(S[rb][i], SCALE == kScaleToken ? cs[i] : coef, -mr);
+    }
+    if (tbase + kPage > lim_lo) {
+      // the page reaches a row's causal limit or the end of the request
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (tbase + wave * 16 + 4 * g + i >= lim[rb]) y[rb][i] = -INFINITY;
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+      ymax[rb] = fmaxf(fmaxf(ymax[rb], fmaxf(y[rb][0], y[rb][1])), fmaxf(y[rb][2], y[rb][3]));
+  };
+  // first page of the split: the reference of each row is its page max
+  auto first_ref = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float pm = group4_max(ymax[rb]);
+      if (g == 0) s_red[wave][rb * 16 + m] = pm;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = rb * 16 + m;
+      m0[rb] = fmaxf(fmaxf(s_red[0][row], s_red[1][row]), fmaxf(s_red[2][row], s_red[3][row]));
+      const float mr = m0[rb] == -INFINITY ? 0.0f : m0[rb];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[rb][i] -= mr;
+      ymax[rb] -= mr;
+    }
+    have_ref = true;
+  };
+  // ---- softmax, part 2: weights 2^y as bf16 P into LDS, the sums, and the
+  // flag that asks for a restart when a weight would exceed 2^64
+  auto weights = [&](int it) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      float e[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(y[rb][i]);
+      uint32_t pk[2];
+      if (SCALE == kScaleToken) {
+        // the per-token V scale rides on the weight; the sums stay unscaled
+#pragma unroll
+        for (int i = 0; i < 2; ++i) pk[i] = pack_bf16x2(e[2 * i] * sc[2 * i], e[2 * i + 1] * sc[2 * i + 1]);
       } else {
 #pragma unroll
-        for (int k0 = 0; k0 < KB; k0 += T::KBATCH) {
-          u32x4 kraw[T::KBATCH];
-#pragma unroll
-          for (int k = 0; k < T::KBATCH; ++k) {
-            const int kb = k0 + k;
-            const int c = 8 * (kb >> 1) + 2 * g + (kb & 1);  // dims 64(kb/2) + 16g + 8(kb&1) .. +8
-            kraw[k] = *reinterpret_cast<const u32x4*>(kv + (tok * Z::NCH + Z::slot(tok, c)) * 16);
-          }
-          __builtin_amdgcn_sched_barrier(0);  // reads ahead of the math
-#pragma unroll
-          for (int k = 0; k < T::KBATCH; ++k)
-            mfma_qk2(S[0], S[1], __builtin_bit_cast(bf16x8, kraw[k]), qop[0][k0 + k], qop[1][k0 + k]);
-        }
+        for (int i = 0; i < 2; ++i) pk[i] = pack_bf16x2(e[2 * i], e[2 * i + 1]);
+        lnrm[rb] = dot2_bf16_ones(pk[1], dot2_bf16_ones(pk[0], lnrm[rb]));
       }
+      lsum[rb] += (e[0] + e[1]) + (e[2] + e[3]);
+      *reinterpret_cast<u32x2*>(s_p[it & 1] + (rb * 16 + m) * T::PSTRIDE + (wave * 16 + 4 * g) * 2) =
+          u32x2{pk[0], pk[1]};
     }
-
-    mfma_result_fence_v(S[0], S[1]);
-
-    // ---- scores in log2 units (lane holds tokens 16w + 4g + i of rows rb*16 + m)
-    float x[2][4];
-    float pmax[2] = {-INFINITY, -INFINITY};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tl = wave * 16 + 4 * g + i;
-      const float c = SCALE == kScaleToken ? coef * s_scale[buf][tl] : coef;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        float v = S[rb][i] * c;
-        if (tbase + tl >= lim[rb]) v = -INFINITY;
-        x[rb][i] = v;
-        pmax[rb] = fmaxf(pmax[rb], v);
-      }
-    }
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      pmax[rb] = group4_max(pmax[rb]);
-      if (g == 0) s_max[wave][rb * 16 + m] = pmax[rb];
-    }
-    if (!have_ref) {
-      // first page of the split: the reference of each row is its page max
-      __syncthreads();
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int row = rb * 16 + m;
-        m0[rb] = fmaxf(fmaxf(s_max[0][row], s_max[1][row]), fmaxf(s_max[2][row], s_max[3][row]));
-      }
-      have_ref = true;
-    }
-    bool over = false;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      over |= pmax[rb] > m0[rb] + kRefSlack;
-      const float mr = m0[rb] == -INFINITY ? 0.0f : m0[rb];
-      uint32_t pb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = x[rb][i];
-        const float e = __builtin_amdgcn_exp2f(v - mr);
-        if (SCALE == kScaleToken) {
-          const float w = v == -INFINITY ? 0.0f : e * s_scale[buf][wave * 16 + 4 * g + i];
-          pb[i] = float_to_bf16(w);
-          lsum[rb] += e;
-        } else {
-          pb[i] = float_to_bf16(e);
-          lsum[rb] += e;
-          lnrm[rb] += float_of(pb[i] << 16);
-        }
-      }
-      u32x2 packed = {pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16)};
-      *reinterpret_cast<u32x2*>(s_p + (rb * 16 + m) * T::PSTRIDE + (wave * 16 + 4 * g) * 2) = packed;
-    }
+    const bool over = ymax[0] > kRefSlack || ymax[1] > kRefSlack;
     const bool any_over = __any(over);
-    if (lane == 0) s_flag[wave] = any_over;
-    __syncthreads();  // P of the page is in LDS
-
-    if ((s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3]) && restarts < kMaxRestarts) {
-      // A weight would exceed 2^64: restart the split with the larger reference.
-      ++restarts;
+    if (lane == 0) s_flag[it & 1][wave] = any_over;
+  };
+  auto flagged = [&](int it) {
+    const int4 f = *reinterpret_cast<const int4*>(&s_flag[it & 1][0]);
+    return (f.x | f.y | f.z | f.w) && restarts < kMaxRestarts;
+  };
+  // A weight would exceed 2^64: restart the split with a reference raised to
+  // each row's running maximum.  Every wave calls this together.
+  auto restart = [&]() {
+    ++restarts;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int row = rb * 16 + m;
-        const float pm = fmaxf(fmaxf(s_max[0][row], s_max[1][row]), fmaxf(s_max[2][row], s_max[3][row]));
-        m0[rb] = fmaxf(m0[rb], pm);
-        lsum[rb] = 0.0f;
-        lnrm[rb] = 0.0f;
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) O[i][j] = mfma_zero();
-      wait_vmcnt<0>();
-      __syncthreads();  // every DMA landed and every wave is past its reads
-      id_chunk = 0;
-      ids = load_ids(p_begin);
-      prologue();
-      p = p_begin - 1;
-      it = -1;
-      continue;
+    for (int rb = 0; rb < 2; ++rb) {
+      const float pm = group4_max(ymax[rb]);
+      if (g == 0) s_red[wave][rb * 16 + m] = pm;
     }
+    wait_vmcnt<0>();
+    __syncthreads();  // every DMA landed, every wave is past its reads, maxima in LDS
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = rb * 16 + m;
+      const float pm = fmaxf(fmaxf(s_red[0][row], s_red[1][row]), fmaxf(s_red[2][row], s_red[3][row]));
+      const float mr = m0[rb] == -INFINITY ? 0.0f : m0[rb];
+      if (pm > -INFINITY) m0[rb] = fmaxf(m0[rb], mr + pm);
+      ymax[rb] = -INFINITY;
+      lsum[rb] = 0.0f;
+      lnrm[rb] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) O[i][j] = mfma_zero();
+    // (s_red is next written at a later restart, past further barriers; the
+    // flags read after a restart are always written after it)
+    id_chunk = 0;
+    ids = load_ids(p_begin);
+    prologue();
+  };
 
-    // ---- O[row][dim] += P V over this wave's 128 dims
-    {
-      const int dim0 = wave * 128;
+  if constexpr (T::PIPE) {
+    // Wait for this wave's own share of page it (the K rows of its 16 tokens),
+    // zero its rows past the end of the request (they may hold anything, even
+    // NaN codes, and P V multiplies them by zero weights), and read its K bytes.
+    auto k_read = [&](int it) {
+      if (it + 1 < n_it)
+        wait_vmcnt<LPP>();
+      else
+        wait_vmcnt<0>();
+      uint8_t* kv = s_kv[it % T::NBUF];
+      const int nvalid = L - (p_begin + it) * kPage;
+      if (nvalid < wave * 16 + 16) {
+        const int t0 = max(nvalid, wave * 16);
+        u32x4* junk = reinterpret_cast<u32x4*>(kv + t0 * T::ROW_BYTES);
+        for (int e = lane; e < (wave * 16 + 16 - t0) * (T::ROW_BYTES / 16); e += 64)
+          junk[e] = u32x4{0u, 0u, 0u, 0u};
+      }
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        // P (rows x 32 tokens) and V operands of this half of the page are read
-        // first, then converted and fed to the MFMAs; the lane's 8 contraction
-        // slots are tokens tok0 .. tok0+7 in both
-        const int tok0 = kt * 32 + g * 8;
-        bf16x8 pop[2];
-        u32x2 vraw[8][CACHE == kFp8 ? 1 : 2];
-#pragma unroll
-        for (int rbp = 0; rbp < 2; ++rbp)
-          pop[rbp] = *reinterpret_cast<const bf16x8*>(s_p + (rbp * 16 + m) * T::PSTRIDE + tok0 * 2);
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          const int dcol = dim0 + db * 16;
-          if constexpr (CACHE == kFp8) {
-            // lane 2j+h of the group addresses token tok0+j, bytes dcol+8h .. +8
-            const int t = tok0 + (m >> 1);
-            vraw[db][0] = lds_read_tr8(kv + (t * Z::NCH + Z::slot(t, dcol >> 4)) * 16 + 8 * (m & 1));
-          } else {
-            // lane 4j+q of the group addresses token tok0+j (+4), elements dcol+4q .. +4
-            const int c = (dcol >> 3) + ((m & 3) >> 1);
-            const int t0 = tok0 + (m >> 2), t1 = t0 + 4;
-            vraw[db][0] = lds_read_tr16(kv + (t0 * Z::NCH + Z::slot(t0, c)) * 16 + 8 * (m & 1));
-            vraw[db][CACHE == kFp8 ? 0 : 1] = lds_read_tr16(kv + (t1 * Z::NCH + Z::slot(t1, c)) * 16 + 8 * (m & 1));
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);  // reads ahead of the math
-        // convert two V blocks into distinct registers, then issue their four MFMAs
-#pragma unroll
-        for (int d0 = 0; d0 < 8; d0 += 2) {
-          bf16x8 vop[2];
-#pragma unroll
-          for (int d = 0; d < 2; ++d) {
-            if constexpr (CACHE == kFp8)
-              vop[d] = e4m3x8_to_bf16x8(vraw[d0 + d][0]);
-            else
-              vop[d] = __builtin_bit_cast(bf16x8, u32x4{vraw[d0 + d][0].x, vraw[d0 + d][0].y,
-                                                        vraw[d0 + d][CACHE == kFp8 ? 0 : 1].x,
-                                                        vraw[d0 + d][CACHE == kFp8 ? 0 : 1].y});
-          }
-#pragma unroll
-          for (int d = 0; d < 2; ++d)
-#pragma unroll
-            for (int rbp = 0; rbp < 2; ++rbp)
-              O[rbp][d0 + d] = mfma_16x16x32_bf16(pop[rbp], vop[d], O[rbp][d0 + d]);
+      for (int i = 0; i < KB / 2; ++i) kraw[i] = *reinterpret_cast<const u32x4*>(kv + klane + 64 * i);
+    };
+    k_read(0);
+    // Iteration it: scores of page it (it < n_it) before the barrier, then
+    // P V of page it - 1 and the softmax weights of page it after it.
+    for (int it = 0; it < n_it + 1; ++it) {
+      const bool has_qk = it < n_it;
+      f32x4 S[2];
+      if (has_qk) qk_fp8(S);
+      __syncthreads();  // P, flags and every wave's share of page it - 1 are in LDS;
+                        // every wave is done with page it - 2 and P of it - 2
+      if (it > 0 && flagged(it - 1)) {
+        restart();
+        k_read(0);
+        it = -1;
+        continue;
+      }
+      const bool next = it + T::DIST < n_it;
+      if (next) {
+        dma_page(it + T::DIST);
+        dma_part(0);
+      }
+      auto mid = [&] { if (next) dma_part(1); };
+      if (it == 0) {
+        mfma_result_fence_v(S[0], S[1]);
+        scores(S, it);
+        if (!have_ref) first_ref();
+      } else {
+        pv(s_kv[(it - 1) % T::NBUF], s_p[(it - 1) & 1], mid);
+        if (has_qk) {
+          // the P V code between puts well over the MFMA result latency
+          // between the score MFMAs and these readers
+          mfma_result_tie_v(S[0], S[1]);
+          scores(S, it);
         }
       }
+      if (has_qk) weights(it);
+      if (next) {
+        if (it == 0) dma_part(1);
+        dma_part(2);
+      }
+      if (it + 1 < n_it) k_read(it + 1);
+    }
+  } else {
+    for (int it = 0; it < n_it; ++it) {
+      wait_vmcnt<0>();
+      __syncthreads();  // page it is in LDS; every wave is done with page it - 1
+      const bool next = it + T::DIST < n_it;
+      if (next) {
+        dma_page(it + T::DIST);
+        dma_part(0);
+        dma_part(1);
+        dma_part(2);
+      }
+      uint8_t* kv = s_kv[it % T::NBUF];
+      const int nvalid = min(kPage, L - (p_begin + it) * kPage);
+      if (nvalid < kPage) {
+        // rows past the end of the request may hold anything (even NaN codes):
+        // zero them so that their zero weights give zero products in PV
+        u32x4* junk = reinterpret_cast<u32x4*>(kv + nvalid * T::ROW_BYTES);
+        for (int e = threadIdx.x; e < (kPage - nvalid) * (T::ROW_BYTES / 16); e += 256)
+          junk[e] = u32x4{0u, 0u, 0u, 0u};
+      }
+      f32x4 S[2];
+      qk_bf16(kv, S);
+      mfma_result_fence_v(S[0], S[1]);
+      scores(S, it);
+      if (!have_ref) first_ref();
+      weights(it);
+      __syncthreads();  // P of the page is in LDS
+      if (flagged(it)) {
+        restart();
+        it = -1;
+        continue;
+      }
+      pv(kv, s_p[it & 1], no_mid);
     }
   }
 
