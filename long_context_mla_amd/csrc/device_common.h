@@ -161,6 +161,80 @@ __device__ __forceinline__ void mfma_result_fence_a(f32x4& r) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(r));
 }
 __device__ __forceinline__ void mfma_result_tie_a(f32x4& r) { asm volatile("" : "+a"(r)); }
+// Hand-ordered building blocks for the FP8 inner loops.  Each is its own
+// volatile asm statement, so the compiler keeps their relative order: MFMAs
+// alternate with pairs of conversions and the conversions issue while the
+// matrix core works.  Wait states: an MFMA that reads a register written by
+// the VALU instruction just before it starts with s_nop 1 (the "_w" forms);
+// elsewhere at least two instructions separate the two.  The compiler does
+// not know the result latency of these MFMAs, so every group of them ends
+// with a result fence on its accumulators before anything else touches them.
+__device__ __forceinline__ uint32_t cvt_e4m3_lo(uint32_t w) {  // bytes 0, 1 -> bf16 x2
+  uint32_t r;
+  asm volatile("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0" : "=v"(r) : "v"(w));
+  return r;
+}
+__device__ __forceinline__ uint32_t cvt_e4m3_hi(uint32_t w) {  // bytes 2, 3 -> bf16 x2
+  uint32_t r;
+  asm volatile("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(r) : "v"(w));
+  return r;
+}
+// C (VGPR) += A (VGPR) * B (AGPR); the first of a chain starts from 0.
+__device__ __forceinline__ void mfma_vva0_w(f32x4& c, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_vva0(f32x4& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_vva_w(f32x4& c, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_vva(f32x4& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+// C (VGPR) += A (VGPR) * B (VGPR).
+__device__ __forceinline__ void mfma_vvv_w(f32x4& c, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vvv(f32x4& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+// Ends a group of hand-placed MFMAs: waits out the matrix pipe and the
+// result latency while the last MFMAs' operands are still held, so that
+// neither their source registers are reused nor their results read early.
+#define MLA_O16(o) "+v"(o[0][0]), "+v"(o[0][1]), "+v"(o[0][2]), "+v"(o[0][3]), "+v"(o[0][4]), "+v"(o[0][5]), \
+    "+v"(o[0][6]), "+v"(o[0][7]), "+v"(o[1][0]), "+v"(o[1][1]), "+v"(o[1][2]), "+v"(o[1][3]),            \
+    "+v"(o[1][4]), "+v"(o[1][5]), "+v"(o[1][6]), "+v"(o[1][7])
+__device__ __forceinline__ void mfma_drain_o(f32x4 (&o)[2][8], bf16x8 a0, bf16x8 a1, bf16x8 b) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : MLA_O16(o) : "v"(a0), "v"(a1), "v"(b));
+}
+__device__ __forceinline__ void mfma_drain_s(f32x4& s0, f32x4& s1, bf16x8 a) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1) : "v"(a));
+}
+// Result fence alone on the sixteen P V accumulators.
+__device__ __forceinline__ void mfma_result_fence_v16(f32x4 (&o)[2][8]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : MLA_O16(o));
+}
+// Zeroes the sixteen P V accumulators in place with MFMAs on zero operands,
+// in one statement that also waits out their latency.
+__device__ __forceinline__ void mfma_zero_o(f32x4 (&o)[2][8]) {
+  const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  asm volatile(
+      "v_mfma_f32_16x16x32_bf16 %0, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %1, %16, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %3, %16, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %4, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %5, %16, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %6, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %7, %16, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %8, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %9, %16, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %10, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %11, %16, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %12, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %13, %16, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %14, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %15, %16, %16, 0\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : MLA_O16(o)
+      : "v"(z));
+}
+__device__ __forceinline__ bf16x8 bf16x8_of(const uint32_t (&d)[4]) {
+  return __builtin_bit_cast(bf16x8, u32x4{d[0], d[1], d[2], d[3]});
+}
 // A value placed in AGPRs (a copy, once); later "a"-constrained uses keep it there.
 __device__ __forceinline__ bf16x8 to_agpr(bf16x8 v) {
   bf16x8 r;

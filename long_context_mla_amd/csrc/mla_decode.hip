@@ -282,11 +282,12 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
   float ymax[2] = {-INFINITY, -INFINITY}; // running max of score - reference, this lane's tokens
   float lsum[2] = {0.0f, 0.0f};          // this lane's share of the softmax sums (fp32 P)
   float lnrm[2] = {0.0f, 0.0f};          // the same over the bf16-rounded P that PV uses
-  f32x4 O[2][8];                          // rows rb*16 + 4g + i, dims 128*wave + 16db + m
+  f32x4 O[2][8];                          // rows rb*16 + 4g + i, dims 128*wave + 16db + m (VGPRs)
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) O[i][j] = mfma_zero();
+    for (int j = 0; j < 8; ++j) O[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  mfma_zero_o(O);
   bool have_ref = false;
   int restarts = 0;
 
@@ -334,24 +335,46 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
         }
       }
       __builtin_amdgcn_sched_barrier(0);  // reads ahead of the math
-      // convert two V blocks into distinct registers, then issue their four MFMAs
+      if constexpr (CACHE == kFp8) {
+        // per 16-dim block: its MFMA pair with the conversions of the next
+        // block between them (two operand register sets)
+        uint32_t d[2][4];
+        d[0][0] = cvt_e4m3_lo(vraw[0][0].x);
+        d[0][1] = cvt_e4m3_hi(vraw[0][0].x);
+        d[0][2] = cvt_e4m3_lo(vraw[0][0].y);
+        d[0][3] = cvt_e4m3_hi(vraw[0][0].y);
 #pragma unroll
-      for (int d0 = 0; d0 < 8; d0 += 2) {
-        bf16x8 vop[2];
+        for (int db = 0; db < 8; ++db) {
+          const bf16x8 vop = bf16x8_of(d[db & 1]);
+          uint32_t (&nx)[4] = d[(db + 1) & 1];
+          mfma_vvv_w(O[0][db], pop[0], vop);
+          if (db + 1 < 8) {
+            nx[0] = cvt_e4m3_lo(vraw[db + 1][0].x);
+            nx[1] = cvt_e4m3_hi(vraw[db + 1][0].x);
+          }
+          mfma_vvv(O[1][db], pop[1], vop);
+          if (db + 1 < 8) {
+            nx[2] = cvt_e4m3_lo(vraw[db + 1][0].y);
+            nx[3] = cvt_e4m3_hi(vraw[db + 1][0].y);
+          }
+        }
+        mfma_drain_o(O, pop[0], pop[1], bf16x8_of(d[1]));
+      } else {
+        // convert two V blocks into distinct registers, then issue their four MFMAs
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          if constexpr (CACHE == kFp8)
-            vop[d] = e4m3x8_to_bf16x8(vraw[d0 + d][0]);
-          else
+        for (int d0 = 0; d0 < 8; d0 += 2) {
+          bf16x8 vop[2];
+#pragma unroll
+          for (int d = 0; d < 2; ++d)
             vop[d] = __builtin_bit_cast(bf16x8, u32x4{vraw[d0 + d][0].x, vraw[d0 + d][0].y,
                                                       vraw[d0 + d][CACHE == kFp8 ? 0 : 1].x,
                                                       vraw[d0 + d][CACHE == kFp8 ? 0 : 1].y});
+#pragma unroll
+          for (int d = 0; d < 2; ++d)
+#pragma unroll
+            for (int rbp = 0; rbp < 2; ++rbp)
+              O[rbp][d0 + d] = mfma_16x16x32_bf16(pop[rbp], vop[d], O[rbp][d0 + d]);
         }
-#pragma unroll
-        for (int d = 0; d < 2; ++d)
-#pragma unroll
-          for (int rbp = 0; rbp < 2; ++rbp)
-            O[rbp][d0 + d] = mfma_16x16x32_bf16(pop[rbp], vop[d], O[rbp][d0 + d]);
       }
     }
   };
@@ -362,24 +385,31 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
   constexpr int KB = kD / 32;
   u32x4 kraw[KB / 2];
   auto qk_fp8 = [&](f32x4 (&S)[2]) {
-    // convert three k-blocks into distinct registers, then issue their six
-    // MFMAs: consecutive MFMAs never wait on a register still being read
+    // One MFMA pair per k-block, the conversions of the next k-block
+    // between them (software pipelined over two operand register sets).
+    auto lo_word = [&](int kb) { const u32x4 w = kraw[kb >> 1]; return (kb & 1) ? w[2] : w[0]; };
+    auto hi_word = [&](int kb) { const u32x4 w = kraw[kb >> 1]; return (kb & 1) ? w[3] : w[1]; };
+    uint32_t d[2][4];
+    d[0][0] = cvt_e4m3_lo(lo_word(0));
+    d[0][1] = cvt_e4m3_hi(lo_word(0));
+    d[0][2] = cvt_e4m3_lo(hi_word(0));
+    d[0][3] = cvt_e4m3_hi(hi_word(0));
 #pragma unroll
-    for (int k0 = 0; k0 < KB; k0 += 3) {
-      bf16x8 kop[3];
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const u32x4 w = kraw[(k0 + k) >> 1];
-        kop[k] = e4m3x8_to_bf16x8(((k0 + k) & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]});
+    for (int kb = 0; kb < KB; ++kb) {
+      const bf16x8 kop = bf16x8_of(d[kb & 1]);
+      uint32_t (&nx)[4] = d[(kb + 1) & 1];
+      if (kb == 0) mfma_vva0_w(S[0], kop, qop[0][0]); else mfma_vva_w(S[0], kop, qop[0][kb]);
+      if (kb + 1 < KB) {
+        nx[0] = cvt_e4m3_lo(lo_word(kb + 1));
+        nx[1] = cvt_e4m3_hi(lo_word(kb + 1));
       }
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        if (k0 + k == 0)
-          mfma_qk2_first(S[0], S[1], kop[k], qop[0][0], qop[1][0]);
-        else
-          mfma_qk2(S[0], S[1], kop[k], qop[0][k0 + k], qop[1][k0 + k]);
+      if (kb == 0) mfma_vva0(S[1], kop, qop[1][0]); else mfma_vva(S[1], kop, qop[1][kb]);
+      if (kb + 1 < KB) {
+        nx[2] = cvt_e4m3_lo(hi_word(kb + 1));
+        nx[3] = cvt_e4m3_hi(hi_word(kb + 1));
       }
     }
+    mfma_drain_s(S[0], S[1], bf16x8_of(d[(KB - 1) & 1]));
   };
   auto qk_bf16 = [&](const uint8_t* kv, f32x4 (&S)[2]) {
 #pragma unroll
@@ -506,10 +536,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
       lsum[rb] = 0.0f;
       lnrm[rb] = 0.0f;
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) O[i][j] = mfma_zero();
+    mfma_zero_o(O);
     // (s_red is next written at a later restart, past further barriers; the
     // flags read after a restart are always written after it)
     id_chunk = 0;
@@ -537,46 +564,58 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < KB / 2; ++i) kraw[i] = *reinterpret_cast<const u32x4*>(kv + klane + 64 * i);
     };
-    k_read(0);
-    // Iteration it: scores of page it (it < n_it) before the barrier, then
-    // P V of page it - 1 and the softmax weights of page it after it.
-    for (int it = 0; it < n_it + 1; ++it) {
-      const bool has_qk = it < n_it;
-      f32x4 S[2];
-      if (has_qk) qk_fp8(S);
-      __syncthreads();  // P, flags and every wave's share of page it - 1 are in LDS;
-                        // every wave is done with page it - 2 and P of it - 2
-      if (it > 0 && flagged(it - 1)) {
-        restart();
-        k_read(0);
-        it = -1;
-        continue;
-      }
-      const bool next = it + T::DIST < n_it;
-      if (next) {
-        dma_page(it + T::DIST);
-        dma_part(0);
-      }
-      auto mid = [&] { if (next) dma_part(1); };
-      if (it == 0) {
-        mfma_result_fence_v(S[0], S[1]);
-        scores(S, it);
-        if (!have_ref) first_ref();
-      } else {
-        pv(s_kv[(it - 1) % T::NBUF], s_p[(it - 1) & 1], mid);
-        if (has_qk) {
-          // the P V code between puts well over the MFMA result latency
-          // between the score MFMAs and these readers
-          mfma_result_tie_v(S[0], S[1]);
-          scores(S, it);
+    // Page it: scores before the barrier; after it, P V of page it - 1 and
+    // the softmax weights of page it.  The first page is peeled off so that
+    // the steady-state loop is a single path; a restart (rare) repeats the
+    // whole split.
+    for (;;) {
+      k_read(0);
+      {
+        f32x4 S[2];
+        qk_fp8(S);
+        __syncthreads();  // every wave past its setup reads
+        const bool next = T::DIST < n_it;
+        if (next) {
+          dma_page(T::DIST);
+          dma_part(0);
+          dma_part(1);
         }
+        scores(S, 0);
+        if (!have_ref) first_ref();
+        weights(0);
+        if (next) dma_part(2);
+        if (1 < n_it) k_read(1);
       }
-      if (has_qk) weights(it);
-      if (next) {
-        if (it == 0) dma_part(1);
-        dma_part(2);
+      bool again = false;
+      for (int it = 1; it < n_it; ++it) {
+        f32x4 S[2];
+        qk_fp8(S);
+        __syncthreads();  // P, flags and every wave's share of page it - 1 are in LDS;
+                          // every wave is done with page it - 2 and P of it - 2
+        if (flagged(it - 1)) {
+          again = true;
+          break;
+        }
+        const bool next = it + T::DIST < n_it;
+        if (next) {
+          dma_page(it + T::DIST);
+          dma_part(0);
+        }
+        pv(s_kv[(it - 1) % T::NBUF], s_p[(it - 1) & 1], [&] { if (next) dma_part(1); });
+        scores(S, it);
+        weights(it);
+        if (next) dma_part(2);
+        if (it + 1 < n_it) k_read(it + 1);
       }
-      if (it + 1 < n_it) k_read(it + 1);
+      if (!again) {
+        __syncthreads();  // P and flags of the last page are in LDS
+        if (flagged(n_it - 1))
+          again = true;
+        else
+          pv(s_kv[(n_it - 1) % T::NBUF], s_p[(n_it - 1) & 1], no_mid);
+      }
+      if (!again) break;
+      restart();
     }
   } else {
     for (int it = 0; it < n_it; ++it) {
@@ -615,6 +654,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
   }
 
   // ---- epilogue: softmax sums across lanes and token groups, then O / l
+  mfma_result_fence_v16(O);
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const float ls = group4_sum(lsum[rb]);
