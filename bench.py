@@ -45,7 +45,24 @@ def parse():
     ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--max-splits", type=int, default=0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes --steps times (the "
+                         "reference reading for HBM traffic counters) and exit")
     return ap.parse_args()
+
+
+def copy_probe(nbytes, steps):
+    """A plain copy of known size: FETCH_SIZE / WRITE_SIZE read under it calibrate
+    the counter units against bytes actually moved."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "launches": steps}), flush=True)
 
 
 def kernel_source_hash():
@@ -115,6 +132,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this decode path has "
               "no multi-GPU mode to benchmark.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, args.steps)
+        return
     import numpy as np
     import torch
 

@@ -380,6 +380,51 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
   };
   auto no_mid = [] {};
 
+  // FP8 P V split in two: pv_read issues every LDS read of a page's P V (both
+  // 32-token halves) so that their latency hides behind other work, pv_math
+  // consumes them.  Operand layouts as in pv above.
+  bf16x8 pv_p[2][2];   // [half][row block]
+  u32x2 pv_v[2][8];    // [half][16-dim block]
+  auto pv_read = [&](const uint8_t* kvp, const uint8_t* pp) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int tok0 = kt * 32 + g * 8;
+#pragma unroll
+      for (int rbp = 0; rbp < 2; ++rbp)
+        pv_p[kt][rbp] = *reinterpret_cast<const bf16x8*>(pp + (rbp * 16 + m) * T::PSTRIDE + tok0 * 2);
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        pv_v[kt][db] = lds_read_tr8(kvp + voff[db & 3] + kt * 32 * T::ROW_BYTES + 64 * (db >> 2));
+    }
+  };
+  auto pv_math = [&](auto mid) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      if (kt == 1) mid();
+      uint32_t d[2][4];
+      d[0][0] = cvt_e4m3_lo(pv_v[kt][0].x);
+      d[0][1] = cvt_e4m3_hi(pv_v[kt][0].x);
+      d[0][2] = cvt_e4m3_lo(pv_v[kt][0].y);
+      d[0][3] = cvt_e4m3_hi(pv_v[kt][0].y);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const bf16x8 vop = bf16x8_of(d[db & 1]);
+        uint32_t (&nx)[4] = d[(db + 1) & 1];
+        mfma_vvv_w(O[0][db], pv_p[kt][0], vop);
+        if (db + 1 < 8) {
+          nx[0] = cvt_e4m3_lo(pv_v[kt][db + 1].x);
+          nx[1] = cvt_e4m3_hi(pv_v[kt][db + 1].x);
+        }
+        mfma_vvv(O[1][db], pv_p[kt][1], vop);
+        if (db + 1 < 8) {
+          nx[2] = cvt_e4m3_lo(pv_v[kt][db + 1].y);
+          nx[3] = cvt_e4m3_hi(pv_v[kt][db + 1].y);
+        }
+      }
+      mfma_drain_o(O, pv_p[kt][0], pv_p[kt][1], bf16x8_of(d[1]));
+    }
+  };
+
   // ---- S^T[token][row] = K Q^T for this wave's 16 tokens of the page, all
   // 32 rows: from the FP8 bytes already read (kraw) or, BF16, from LDS
   constexpr int KB = kD / 32;
@@ -564,55 +609,59 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < KB / 2; ++i) kraw[i] = *reinterpret_cast<const u32x4*>(kv + klane + 64 * i);
     };
-    // Page it: scores before the barrier; after it, P V of page it - 1 and
-    // the softmax weights of page it.  The first page is peeled off so that
-    // the steady-state loop is a single path; a restart (rare) repeats the
-    // whole split.
+    // Iteration it: after the barrier, the LDS reads of P V of page it - 1 are
+    // issued first; the scores of page it (K already in registers) cover their
+    // latency; then P V of page it - 1, the K reads of page it + 1 and the
+    // softmax weights of page it.  The first page is peeled off so that the
+    // steady-state loop is a single path; a restart (rare) repeats the split.
     for (;;) {
       k_read(0);
       {
-        f32x4 S[2];
-        qk_fp8(S);
-        __syncthreads();  // every wave past its setup reads
         const bool next = T::DIST < n_it;
         if (next) {
           dma_page(T::DIST);
           dma_part(0);
           dma_part(1);
         }
+        f32x4 S[2];
+        qk_fp8(S);
+        if (1 < n_it) k_read(1);
         scores(S, 0);
         if (!have_ref) first_ref();
         weights(0);
         if (next) dma_part(2);
-        if (1 < n_it) k_read(1);
       }
       bool again = false;
       for (int it = 1; it < n_it; ++it) {
-        f32x4 S[2];
-        qk_fp8(S);
         __syncthreads();  // P, flags and every wave's share of page it - 1 are in LDS;
                           // every wave is done with page it - 2 and P of it - 2
-        if (flagged(it - 1)) {
-          again = true;
-          break;
-        }
+        const int4 fl = *reinterpret_cast<const int4*>(&s_flag[(it - 1) & 1][0]);
+        pv_read(s_kv[(it - 1) % T::NBUF], s_p[(it - 1) & 1]);
         const bool next = it + T::DIST < n_it;
         if (next) {
           dma_page(it + T::DIST);
           dma_part(0);
         }
-        pv(s_kv[(it - 1) % T::NBUF], s_p[(it - 1) & 1], [&] { if (next) dma_part(1); });
+        f32x4 S[2];
+        qk_fp8(S);
+        if ((fl.x | fl.y | fl.z | fl.w) && restarts < kMaxRestarts) {
+          again = true;
+          break;
+        }
+        pv_math([&] { if (next) dma_part(1); });
+        if (it + 1 < n_it) k_read(it + 1);
         scores(S, it);
         weights(it);
         if (next) dma_part(2);
-        if (it + 1 < n_it) k_read(it + 1);
       }
       if (!again) {
         __syncthreads();  // P and flags of the last page are in LDS
-        if (flagged(n_it - 1))
+        if (flagged(n_it - 1)) {
           again = true;
-        else
-          pv(s_kv[(n_it - 1) % T::NBUF], s_p[(n_it - 1) & 1], no_mid);
+        } else {
+          pv_read(s_kv[(n_it - 1) % T::NBUF], s_p[(n_it - 1) & 1]);
+          pv_math(no_mid);
+        }
       }
       if (!again) break;
       restart();
