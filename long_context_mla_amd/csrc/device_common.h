@@ -192,7 +192,13 @@ __device__ __forceinline__ void mfma_vva_w(f32x4& c, bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void mfma_vva(f32x4& c, bf16x8 a, bf16x8 b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
 }
-// C (VGPR) += A (VGPR) * B (VGPR).
+// C (VGPR) += A (VGPR) * B (VGPR); the "0" forms start a chain from 0.
+__device__ __forceinline__ void mfma_vvv0_w(f32x4& c, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_vvv0(f32x4& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
 __device__ __forceinline__ void mfma_vvv_w(f32x4& c, bf16x8 a, bf16x8 b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }

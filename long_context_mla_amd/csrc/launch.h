@@ -44,6 +44,7 @@ int decode_rows_per_group(int B, int R);
 
 hipError_t launch_kv_append(const AppendArgs& a, int scale_mode, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int cache_kind, int scale_mode, hipStream_t stream);
+hipError_t launch_decode_fp8(const DecodeArgs& a, int scale_mode, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 }  // namespace mla

@@ -1,0 +1,538 @@
+// mla_decode_paged, FP8 cache: split-KV decode attention with specialised
+// waves.  Computes what mla_decode.hip describes (one 576-element latent row
+// per token as key and value, "How to serve trillions of tokens for
+// trillion-parameter coding agents", sections "First, understand the workload"
+// and "Tensor parallel was the best parallelism strategy for maximum
+// interactivity"; an e4m3 cache converted as it is read, "Smaller, faster,
+// safer: running Kimi and GLM at scale", section "Quantizing the KV cache").
+//
+// gfx950 design: one 512-thread workgroup (8 waves, two per SIMD) per
+// (request, split, group of 32 query rows), one per CU.  The two waves of a
+// SIMD do different work on different pages, so that one's stalls (LDS
+// latency, conversions, the softmax) are covered by the other's MFMAs:
+//  * score waves 0..3: wave w copies tokens 16w..16w+15 of each page HBM ->
+//    LDS (LDS-DMA), computes their scores S^T = K Q^T for all 32 rows
+//    (query held in VGPRs), the softmax weights P (bf16, into LDS) and the sums;
+//  * output waves 4..7: wave 4+j accumulates O[32 rows][128j .. 128j+127] +=
+//    P V over the previous page, V being the first 512 columns of the same
+//    staged rows (transposing LDS reads).
+// One barrier per page separates "scores of page p" from "P V of page p".
+// The two roles run separate loops with the same sequence of barriers, so the
+// query (score waves) and the accumulators (output waves) never need registers
+// at the same time.  Two waves per SIMD leave 256 registers per wave; the
+// kernel uses VGPRs only (no AGPRs), so all 256 are available to either role.
+//
+// Softmax: one fixed reference per row and split (the first page's maximum),
+// weights 2^(y - m0); a weight above 2^64 restarts the split with a larger
+// reference (all waves together).  The output divides by the sum of the bf16
+// weights that P V used; the LSE uses the exact fp32 sum.
+#include "decode_tile.h"
+#include "device_common.h"
+#include "launch.h"
+
+namespace mla {
+
+template <int SCALE>
+__global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
+  using T = Tile<kFp8>;
+  using Z = Swz<kFp8>;
+  static_assert(T::NBUF == 4 && T::DIST == 2, "four page buffers, two pages in flight");
+  __shared__ __attribute__((aligned(16))) uint8_t s_kv[T::NBUF][T::PAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) float s_scale[T::NBUF][kPage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_p[2][kRows * T::PSTRIDE];
+  __shared__ float s_red[4][kRows];   // per-score-wave row maxima (first page, restarts)
+  __shared__ float s_lsum[4][kRows];
+  __shared__ float s_lnrm[4][kRows];
+  __shared__ float s_m0[kRows];
+  __shared__ __attribute__((aligned(16))) int s_flag[2][4];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool scorer = wave < 4;
+  const int qw = wave & 3;  // index within the role
+  const int m = lane & 15, g = lane >> 4;
+  // Workgroup -> (split, row group): the row groups of one split (which read
+  // the same pages) go to the same XCD back to back and share its L2.
+  const int b = blockIdx.y;
+  const int xcd = blockIdx.x & 7;
+  const int kx = blockIdx.x >> 3;
+  const int rg = kx % a.n_rg;
+  const int split = (kx / a.n_rg) * 8 + xcd;
+  if (split >= a.max_splits) return;
+  const int L = min(max(load_const(a.seq_lens, b), 0), a.max_blocks * kPage);
+  const int n_pages = (L + kPage - 1) / kPage;
+  const int r0 = rg * kRows;
+  const int p_begin = split * a.pps;
+
+  if (p_begin >= n_pages) {
+    // Nothing to read.  Only an empty request's first split reports it; the
+    // combine never reads splits past a request's last page.
+    if (n_pages == 0 && split == 0) {
+      for (int e = threadIdx.x; e < kRows * kDV; e += 512) {
+        const int r = r0 + e / kDV;
+        if (r >= a.R) break;
+        if (a.max_splits == 1)
+          a.out[((int64_t)b * a.R + r) * kDV + e % kDV] = 0;
+        else
+          a.o_part[((int64_t)b * a.max_splits * a.R + r) * kDV + e % kDV] = 0.0f;
+      }
+      for (int r = r0 + threadIdx.x; r < min(r0 + kRows, a.R); r += 512) {
+        if (a.max_splits == 1)
+          a.lse[(int64_t)b * a.R + r] = -INFINITY;
+        else
+          a.lse_part[(int64_t)b * a.max_splits * a.R + r] = -INFINITY;
+      }
+    }
+    return;
+  }
+  const int p_end = split == a.max_splits - 1 ? n_pages : min(n_pages, p_begin + a.pps);
+  const int n_it = p_end - p_begin;
+  const float tscale = SCALE == kScaleTensor ? load_const(a.kv_scale, 0) : 1.0f;
+  bool have_ref = false;
+  int restarts = 0;
+  auto flagged = [&](int it) {
+    const int4 f = *reinterpret_cast<const int4*>(&s_flag[it & 1][0]);
+    return (f.x | f.y | f.z | f.w) && restarts < kMaxRestarts;
+  };
+
+  if (scorer) {
+    // =====================================================================
+    // score waves
+    // =====================================================================
+    const float coef = a.sm_log2 * tscale;
+    constexpr int QBUF = T::NBUF - 1;
+    // The query of the group's 32 rows, HBM -> LDS in one coalesced copy
+    // shared by the four score waves, into the page buffer that stays free
+    // until the third page copy.  Row r's 16-byte chunk c (72 per row) goes to
+    // slot r * 72 + (c ^ ((r / 2) % 8)), which makes the operand reads below
+    // free of bank conflicts.  Rows past R repeat row R - 1 (results dropped).
+    const uint32_t qlds = lds_addr(&s_kv[QBUF][0]);
+#pragma unroll
+    for (int j = 0; j < 9; ++j) {
+      const int slot = (qw * 9 + j) * 64 + lane;  // 2304 slots = 32 rows x 72 chunks
+      const int r = slot / 72;
+      const int c = (slot - r * 72) ^ ((r >> 1) & 7);
+      const uint16_t* src = a.q + ((int64_t)b * a.R + min(r0 + r, a.R - 1)) * kD + c * 8;
+      lds_dma16_lane(src, qlds + (qw * 9 + j) * 1024);
+    }
+
+    // Page ids of the split, 64 at a time, one per lane; picked out with
+    // readlane so the DMA issue never waits on a scalar load.
+    const int64_t bt_row = (int64_t)b * a.max_blocks;
+    auto load_ids = [&](int first) {
+      const int idx = first + lane;
+      int pg = idx < p_end ? a.block_table[bt_row + idx] : 0;
+      return min(max(pg, 0), a.num_pages - 1);
+    };
+    int id_chunk = 0;
+    int ids = load_ids(p_begin);
+
+    // causal limit of this lane's rows rb*16 + m: row i*H + h sees tokens
+    // t < L - n_q + i + 1; lim_lo is the first token any real row of the group
+    // masks, so earlier pages need no mask (rows past R only pad the group)
+    int lim[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = r0 + rb * 16 + m;
+      lim[rb] = row < a.R ? L - a.n_q + row / a.H + 1 : 0;
+    }
+    const int lim_lo = L - a.n_q + r0 / a.H + 1;
+
+    constexpr int LPP = T::LOADS + (SCALE == kScaleToken ? 1 : 0);  // loads per page per wave
+    // each lane's source offsets inside a page for its LOADS LDS chunk slots;
+    // wave w copies tokens 16w .. 16w+15, the rows its own QK^T reads
+    uint32_t goff[T::LOADS];
+#pragma unroll
+    for (int j = 0; j < T::LOADS; ++j) {
+      const int slot = (qw * T::LOADS + j) * 64 + lane;
+      const int t = slot / Z::NCH;
+      goff[j] = t * T::ROW_BYTES + Z::chunk_of_slot(t, slot - t * Z::NCH) * 16;
+    }
+    const uint8_t* dma_src = a.cache;
+    uint32_t dma_dst = 0;
+    auto dma_page = [&](int it) {  // select page p_begin + it for the following dma_part calls
+      if ((it >> 6) != id_chunk) {
+        id_chunk = it >> 6;
+        ids = load_ids(p_begin + (id_chunk << 6));
+      }
+      const int pg = __builtin_amdgcn_readlane(ids, it & 63);
+      dma_src = a.cache + (int64_t)pg * T::PAGE_BYTES;
+      dma_dst = lds_addr(&s_kv[it % T::NBUF][0]) + qw * T::LOADS * 1024;
+      if (SCALE == kScaleToken)
+        lds_dma4(a.kv_scale + (int64_t)pg * kPage, lane * 4, lds_addr(&s_scale[it % T::NBUF][0]));
+    };
+    auto dma_part = [&](int part) {
+#pragma unroll
+      for (int j = 0; j < T::LOADS; ++j)
+        if (j / T::PART == part) lds_dma16(dma_src, goff[j], dma_dst + j * 1024);
+    };
+    auto prologue = [&]() {
+#pragma unroll
+      for (int k = 0; k < T::DIST; ++k)
+        if (k < n_it) {
+          dma_page(k);
+          dma_part(0);
+          dma_part(1);
+          dma_part(2);
+        }
+    };
+    prologue();
+
+    // Query operands LDS -> VGPRs: lane (m, g) holds rows rb*16 + m and, for
+    // k-block kb, dims 64(kb/2) + 16g + 8(kb%2) .. +8; k-blocks 2i and 2i+1
+    // take the 16 consecutive dims of one 16-byte FP8 chunk of K.
+    if (n_it >= 2)
+      wait_vmcnt<2 * LPP>();
+    else
+      wait_vmcnt<LPP>();
+    __syncthreads();  // (1) every score wave's share of the query is in LDS
+    bf16x8 qop[2][kD / 32];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = rb * 16 + m;
+#pragma unroll
+      for (int kb = 0; kb < kD / 32; ++kb) {
+        const int c = 8 * (kb >> 1) + 2 * g + (kb & 1);
+        qop[rb][kb] = *reinterpret_cast<const bf16x8*>(&s_kv[QBUF][(row * 72 + (c ^ ((row >> 1) & 7))) * 16]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the query buffer may be overwritten
+
+    float m0[2] = {-INFINITY, -INFINITY};   // log2-domain reference of this lane's rows
+    float ymax[2] = {-INFINITY, -INFINITY};  // running max of score - reference
+    float lsum[2] = {0.0f, 0.0f};           // this lane's share of the softmax sums (fp32 P)
+    float lnrm[2] = {0.0f, 0.0f};           // the same over the bf16-rounded P that PV uses
+    const int tok = qw * 16 + m;            // this lane's token in QK^T
+    const uint32_t klane = (uint32_t)((tok * Z::NCH + Z::slot(tok, g)) * 16);
+    constexpr int KB = kD / 32;
+    u32x4 kraw[KB / 2];  // this wave's K bytes of the next page, read ahead
+
+    // Wait for this wave's own share of page it, zero its rows past the end of
+    // the request (they may hold anything, even NaN codes, and P V multiplies
+    // them by zero weights), and read its K bytes.
+    auto k_read = [&](int it) {
+      if (it + 1 < n_it)
+        wait_vmcnt<LPP>();
+      else
+        wait_vmcnt<0>();
+      uint8_t* kv = s_kv[it % T::NBUF];
+      const int nvalid = L - (p_begin + it) * kPage;
+      if (nvalid < qw * 16 + 16) {
+        const int t0 = max(nvalid, qw * 16);
+        u32x4* junk = reinterpret_cast<u32x4*>(kv + t0 * T::ROW_BYTES);
+        for (int e = lane; e < (qw * 16 + 16 - t0) * (T::ROW_BYTES / 16); e += 64)
+          junk[e] = u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < KB / 2; ++i) kraw[i] = *reinterpret_cast<const u32x4*>(kv + klane + 64 * i);
+    };
+    // S^T[token][row] = K Q^T for this wave's 16 tokens, all 32 rows: one MFMA
+    // pair per k-block with the conversions of the next k-block between them.
+    auto qk = [&](f32x4 (&S)[2]) {
+      auto lo_word = [&](int kb) { const u32x4 w = kraw[kb >> 1]; return (kb & 1) ? w[2] : w[0]; };
+      auto hi_word = [&](int kb) { const u32x4 w = kraw[kb >> 1]; return (kb & 1) ? w[3] : w[1]; };
+      uint32_t d[2][4];
+      d[0][0] = cvt_e4m3_lo(lo_word(0));
+      d[0][1] = cvt_e4m3_hi(lo_word(0));
+      d[0][2] = cvt_e4m3_lo(hi_word(0));
+      d[0][3] = cvt_e4m3_hi(hi_word(0));
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 kop = bf16x8_of(d[kb & 1]);
+        uint32_t (&nx)[4] = d[(kb + 1) & 1];
+        if (kb == 0) mfma_vvv0_w(S[0], kop, qop[0][0]); else mfma_vvv_w(S[0], kop, qop[0][kb]);
+        if (kb + 1 < KB) {
+          nx[0] = cvt_e4m3_lo(lo_word(kb + 1));
+          nx[1] = cvt_e4m3_hi(lo_word(kb + 1));
+        }
+        if (kb == 0) mfma_vvv0(S[1], kop, qop[1][0]); else mfma_vvv(S[1], kop, qop[1][kb]);
+        if (kb + 1 < KB) {
+          nx[2] = cvt_e4m3_lo(hi_word(kb + 1));
+          nx[3] = cvt_e4m3_hi(hi_word(kb + 1));
+        }
+      }
+      mfma_drain_s(S[0], S[1], bf16x8_of(d[(KB - 1) & 1]));
+    };
+    // softmax, part 1: y = score * coef - reference (log2 units), masked past
+    // each row's causal limit, and the running maxima.  Lane holds tokens
+    // 16w + 4g + i of rows rb*16 + m.
+    float y[2][4];
+    f32x4 sc = {1.0f, 1.0f, 1.0f, 1.0f};
+    auto scores = [&](const f32x4 (&S)[2], int it) {
+      const int tbase = (p_begin + it) * kPage;
+      float cs[4];
+      if (SCALE == kScaleToken) {
+        sc = *reinterpret_cast<const f32x4*>(&s_scale[it % T::NBUF][qw * 16 + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cs[i] = coef * sc[i];
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const float mr = m0[rb] == -INFINITY ? 0.0f : m0[rb];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          y[rb][i] = __builtin_fmaf(S[rb][i], SCALE == kScaleToken ? cs[i] : coef, -mr);
+      }
+      if (tbase + kPage > lim_lo) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (tbase + qw * 16 + 4 * g + i >= lim[rb]) y[rb][i] = -INFINITY;
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        ymax[rb] = fmaxf(fmaxf(ymax[rb], fmaxf(y[rb][0], y[rb][1])), fmaxf(y[rb][2], y[rb][3]));
+    };
+    // softmax, part 2: weights 2^y as bf16 P into LDS, the sums, and the flag
+    // that asks for a restart when a weight would exceed 2^64
+    auto weights = [&](int it) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(y[rb][i]);
+        uint32_t pk[2];
+        if (SCALE == kScaleToken) {
+          // the per-token V scale rides on the weight; the sums stay unscaled
+#pragma unroll
+          for (int i = 0; i < 2; ++i) pk[i] = pack_bf16x2(e[2 * i] * sc[2 * i], e[2 * i + 1] * sc[2 * i + 1]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) pk[i] = pack_bf16x2(e[2 * i], e[2 * i + 1]);
+          lnrm[rb] = dot2_bf16_ones(pk[1], dot2_bf16_ones(pk[0], lnrm[rb]));
+        }
+        lsum[rb] += (e[0] + e[1]) + (e[2] + e[3]);
+        *reinterpret_cast<u32x2*>(s_p[it & 1] + (rb * 16 + m) * T::PSTRIDE + (qw * 16 + 4 * g) * 2) =
+            u32x2{pk[0], pk[1]};
+      }
+      const bool over = ymax[0] > kRefSlack || ymax[1] > kRefSlack;
+      const bool any_over = __any(over);
+      if (lane == 0) s_flag[it & 1][qw] = any_over;
+    };
+
+    for (;;) {
+      k_read(0);
+      {
+        // page 0 (the first page of an attempt)
+        const bool next = T::DIST < n_it;
+        if (next) {
+          dma_page(T::DIST);
+          dma_part(0);
+          dma_part(1);
+        }
+        f32x4 S[2];
+        qk(S);
+        if (1 < n_it) k_read(1);
+        scores(S, 0);
+        if (!have_ref) {
+          // the reference of each row is its maximum over the first page
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            const float pm = group4_max(ymax[rb]);
+            if (g == 0) s_red[qw][rb * 16 + m] = pm;
+          }
+          __syncthreads();  // (2) first-page maxima in LDS
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            const int row = rb * 16 + m;
+            m0[rb] = fmaxf(fmaxf(s_red[0][row], s_red[1][row]), fmaxf(s_red[2][row], s_red[3][row]));
+            const float mr = m0[rb] == -INFINITY ? 0.0f : m0[rb];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[rb][i] -= mr;
+            ymax[rb] -= mr;
+          }
+          have_ref = true;
+        }
+        weights(0);
+        if (next) dma_part(2);
+      }
+      __syncthreads();  // (3) P and flags of page 0 are in LDS
+      bool again = flagged(0);
+      for (int it = 1; it < n_it && !again; ++it) {
+        const bool next = it + T::DIST < n_it;
+        if (next) {
+          dma_page(it + T::DIST);
+          dma_part(0);
+        }
+        f32x4 S[2];
+        qk(S);
+        if (next) dma_part(1);
+        if (it + 1 < n_it) k_read(it + 1);
+        scores(S, it);
+        weights(it);
+        if (next) dma_part(2);
+        __syncthreads();  // (4) P and flags of page it are in LDS; page it - 1 is consumed
+        again = flagged(it);
+      }
+      if (!again) break;
+      // A weight would exceed 2^64: restart the split with a reference raised
+      // to each row's running maximum.
+      ++restarts;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const float pm = group4_max(ymax[rb]);
+        if (g == 0) s_red[qw][rb * 16 + m] = pm;
+      }
+      wait_vmcnt<0>();
+      __syncthreads();  // (5) every copy landed, the maxima are in LDS
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int row = rb * 16 + m;
+        const float pm = fmaxf(fmaxf(s_red[0][row], s_red[1][row]), fmaxf(s_red[2][row], s_red[3][row]));
+        const float mr = m0[rb] == -INFINITY ? 0.0f : m0[rb];
+        if (pm > -INFINITY) m0[rb] = fmaxf(m0[rb], mr + pm);
+        ymax[rb] = -INFINITY;
+        lsum[rb] = 0.0f;
+        lnrm[rb] = 0.0f;
+      }
+      id_chunk = 0;
+      ids = load_ids(p_begin);
+      prologue();
+    }
+    // the sums of this wave's tokens for the output waves
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float ls = group4_sum(lsum[rb]);
+      const float ln = SCALE == kScaleToken ? ls : group4_sum(lnrm[rb]);
+      const int row = rb * 16 + m;
+      if (g == 0) {
+        s_lsum[qw][row] = ls;
+        s_lnrm[qw][row] = ln;
+        if (qw == 0) s_m0[row] = m0[rb];
+      }
+    }
+    __syncthreads();  // (6) sums in LDS
+  } else {
+    // =====================================================================
+    // output waves: the same barrier sequence, P V one page behind
+    // =====================================================================
+    f32x4 O[2][8];  // rows rb*16 + 4g + i, dims 128*qw + 16db + m (VGPRs)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) O[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mfma_zero_o(O);
+    // per-lane LDS offsets of the V reads: lane 2j+h of a 16-lane group
+    // addresses token 8g+j (+32 kt) of its wave's dims; the chunk slot of dims
+    // 128w + 64(db/4) + 16(db%4) is 8w + 4(db/4) + ((db%4) ^ f), f = (token/4)%4
+    uint32_t voff[4];
+    {
+      const int t = g * 8 + (m >> 1);
+      const int f = (t >> 2) & 3;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb)
+        voff[bb] = (uint32_t)((t * Z::NCH + qw * 8 + (bb ^ f)) * 16 + 8 * (m & 1));
+    }
+    bf16x8 pv_p[2][2];  // [32-token half][row block]
+    u32x2 pv_v[2][8];   // [32-token half][16-dim block]
+    auto pv = [&](int it) {
+      const uint8_t* kvp = s_kv[it % T::NBUF];
+      const uint8_t* pp = s_p[it & 1];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int tok0 = kt * 32 + g * 8;
+#pragma unroll
+        for (int rbp = 0; rbp < 2; ++rbp)
+          pv_p[kt][rbp] = *reinterpret_cast<const bf16x8*>(pp + (rbp * 16 + m) * T::PSTRIDE + tok0 * 2);
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+          pv_v[kt][db] = lds_read_tr8(kvp + voff[db & 3] + kt * 32 * T::ROW_BYTES + 64 * (db >> 2));
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        uint32_t d[2][4];
+        d[0][0] = cvt_e4m3_lo(pv_v[kt][0].x);
+        d[0][1] = cvt_e4m3_hi(pv_v[kt][0].x);
+        d[0][2] = cvt_e4m3_lo(pv_v[kt][0].y);
+        d[0][3] = cvt_e4m3_hi(pv_v[kt][0].y);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const bf16x8 vop = bf16x8_of(d[db & 1]);
+          uint32_t (&nx)[4] = d[(db + 1) & 1];
+          mfma_vvv_w(O[0][db], pv_p[kt][0], vop);
+          if (db + 1 < 8) {
+            nx[0] = cvt_e4m3_lo(pv_v[kt][db + 1].x);
+            nx[1] = cvt_e4m3_hi(pv_v[kt][db + 1].x);
+          }
+          mfma_vvv(O[1][db], pv_p[kt][1], vop);
+          if (db + 1 < 8) {
+            nx[2] = cvt_e4m3_lo(pv_v[kt][db + 1].y);
+            nx[3] = cvt_e4m3_hi(pv_v[kt][db + 1].y);
+          }
+        }
+        mfma_drain_o(O, pv_p[kt][0], pv_p[kt][1], bf16x8_of(d[1]));
+      }
+    };
+
+    __syncthreads();  // (1)
+    for (;;) {
+      if (!have_ref) {
+        __syncthreads();  // (2)
+        have_ref = true;
+      }
+      __syncthreads();  // (3)
+      bool again = flagged(0);
+      for (int it = 1; it < n_it && !again; ++it) {
+        pv(it - 1);
+        __syncthreads();  // (4)
+        again = flagged(it);
+      }
+      if (!again) {
+        pv(n_it - 1);
+        break;
+      }
+      ++restarts;
+      __syncthreads();  // (5)
+      mfma_zero_o(O);
+    }
+
+    __syncthreads();  // (6) the score waves' sums are in LDS
+    const int dim0 = qw * 128;
+#pragma unroll
+    for (int rbp = 0; rbp < 2; ++rbp)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = rbp * 16 + 4 * g + i;
+        const int r = r0 + row;
+        if (r >= a.R) continue;
+        const float lt = s_lsum[0][row] + s_lsum[1][row] + s_lsum[2][row] + s_lsum[3][row];
+        const float ln = s_lnrm[0][row] + s_lnrm[1][row] + s_lnrm[2][row] + s_lnrm[3][row];
+        // the output is a weighted mean with the bf16 weights PV used; the LSE
+        // uses the fp32 weights
+        const float inv = ln > 0.0f ? tscale / ln : 0.0f;
+        const float mr = s_m0[row] == -INFINITY ? 0.0f : s_m0[row];
+        const float lse_nat = lt > 0.0f ? (mr + __log2f(lt)) * kLn2 : -INFINITY;
+        if (a.max_splits == 1) {
+          uint16_t* dst = a.out + ((int64_t)b * a.R + r) * kDV + dim0 + m;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) dst[db * 16] = float_to_bf16(O[rbp][db][i] * inv);
+          if (qw == 0 && m == 0) a.lse[(int64_t)b * a.R + r] = lse_nat;
+        } else {
+          const int64_t pr = ((int64_t)b * a.max_splits + split) * a.R + r;
+          float* dst = a.o_part + pr * kDV + dim0 + m;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) dst[db * 16] = O[rbp][db][i] * inv;
+          if (qw == 0 && m == 0) a.lse_part[pr] = lse_nat;
+        }
+      }
+  }
+}
+
+hipError_t launch_decode_fp8(const DecodeArgs& a, int scale_mode, hipStream_t stream) {
+  const dim3 grid(((a.max_splits + 7) / 8) * 8 * a.n_rg, a.B), block(512);
+  switch (scale_mode) {
+    case kScaleTensor:
+      hipLaunchKernelGGL((decode_fp8_kernel<kScaleTensor>), grid, block, 0, stream, a);
+      break;
+    case kScaleToken:
+      hipLaunchKernelGGL((decode_fp8_kernel<kScaleToken>), grid, block, 0, stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL((decode_fp8_kernel<kScaleNone>), grid, block, 0, stream, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mla
