@@ -108,8 +108,10 @@ int kv_append_fp8(const void* kv_new, void* kv_cache, float* kv_scale, int scale
  *   pages_per_split, max_splits  the split-KV plan (mla_decode_plan gives one):
  *               split s of request b covers pages [s*pps, (s+1)*pps), except
  *               that split max_splits-1 also takes every page after it.
- *   o_partial   fp32 [B, max_splits, n_q, H, 512]: per-split output,
- *               normalised by the split's own softmax sum.
+ *   o_partial   bf16 [B, max_splits, n_q, H, 512]: per-split output,
+ *               normalised by the split's own softmax sum (rounded to bf16:
+ *               the partials are read back once, and their rounding is far
+ *               inside the output tolerance).
  *   lse_partial fp32 [B, max_splits, n_q, H]: per-split natural log-sum-exp
  *               (-inf for a row that sees no token of the split).
  *   out         bf16 [B, n_q, H, 512];  lse  fp32 [B, n_q, H] (natural log).
@@ -124,7 +126,7 @@ int kv_append_fp8(const void* kv_new, void* kv_cache, float* kv_scale, int scale
 int mla_decode_paged(const void* q, const void* kv_cache, int cache_dtype, const float* kv_scale,
                      int scale_mode, const int32_t* block_table, const int32_t* seq_lens, int B,
                      int n_q, int H, int max_blocks, int num_pages, float softmax_scale,
-                     int pages_per_split, int max_splits, float* o_partial, float* lse_partial,
+                     int pages_per_split, int max_splits, void* o_partial, float* lse_partial,
                      void* out, float* lse, void* stream);
 
 /*
@@ -138,7 +140,7 @@ int mla_decode_paged(const void* q, const void* kv_cache, int cache_dtype, const
  * Same shapes as mla_decode_paged; pages_per_split and max_splits must be the
  * values that call used.
  */
-int mla_decode_combine(const float* o_partial, const float* lse_partial, const int32_t* seq_lens,
+int mla_decode_combine(const void* o_partial, const float* lse_partial, const int32_t* seq_lens,
                        int B, int n_q, int H, int max_blocks, int pages_per_split, int max_splits,
                        void* out, float* lse, void* stream);
 

@@ -135,7 +135,7 @@ def mla_decode_paged(q, kv_cache, kv_scale, scale_mode, block_table, seq_lens, s
                      lse=None, stream=None):
     """q bf16 [B, n_q, H, 576]; kv_cache E4M3 codes (uint8) or bf16 [num_pages, 64, 576].
     With max_splits == 1 writes out bf16 [B, n_q, H, 512] and lse fp32 [B, n_q, H];
-    otherwise o_partial fp32 [B, max_splits, n_q, H, 512] and lse_partial fp32
+    otherwise o_partial bf16 [B, max_splits, n_q, H, 512] and lse_partial fp32
     [B, max_splits, n_q, H]."""
     mode = _SCALE_NAMES[scale_mode] if isinstance(scale_mode, str) else int(scale_mode)
     dev = q.device
@@ -158,7 +158,7 @@ def mla_decode_paged(q, kv_cache, kv_scale, scale_mode, block_table, seq_lens, s
         if tuple(out.shape) != (B, n_q, H, VALUE_DIM) or tuple(lse.shape) != (B, n_q, H):
             raise ValueError("out / lse shape mismatch")
     else:
-        _need(o_partial, "o_partial", torch.float32, dev)
+        _need(o_partial, "o_partial", torch.bfloat16, dev)
         _need(lse_partial, "lse_partial", torch.float32, dev)
         if tuple(o_partial.shape) != (B, max_splits, n_q, H, VALUE_DIM) or \
                 tuple(lse_partial.shape) != (B, max_splits, n_q, H):
@@ -176,7 +176,7 @@ def mla_decode_combine(o_partial, lse_partial, seq_lens, max_blocks, pages_per_s
                        stream=None):
     """Merge the partials of mla_decode_paged into out bf16 [B, n_q, H, 512] and lse fp32 [B, n_q, H]."""
     dev = o_partial.device
-    _need(o_partial, "o_partial", torch.float32, dev, 5)
+    _need(o_partial, "o_partial", torch.bfloat16, dev, 5)
     _need(lse_partial, "lse_partial", torch.float32, dev, 4)
     _need(seq_lens, "seq_lens", torch.int32, dev, 1)
     _need(out, "out", torch.bfloat16, dev, 4)

@@ -64,7 +64,7 @@ int kv_append_fp8(const void* kv_new, void* kv_cache, float* kv_scale, int scale
 int mla_decode_paged(const void* q, const void* kv_cache, int cache_dtype, const float* kv_scale,
                      int scale_mode, const int32_t* block_table, const int32_t* seq_lens, int B,
                      int n_q, int H, int max_blocks, int num_pages, float softmax_scale,
-                     int pages_per_split, int max_splits, float* o_partial, float* lse_partial,
+                     int pages_per_split, int max_splits, void* o_partial, float* lse_partial,
                      void* out, float* lse, void* stream) {
   if (int s = check_cache_mode(cache_dtype, scale_mode)) return s;
   if (bad_stream_free_shape(B, n_q, H)) return MLA_ERR_BAD_SHAPE;
@@ -86,7 +86,7 @@ int mla_decode_paged(const void* q, const void* kv_cache, int cache_dtype, const
   a.kv_scale = kv_scale;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
-  a.o_part = o_partial;
+  a.o_part = static_cast<uint16_t*>(o_partial);
   a.lse_part = lse_partial;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
@@ -105,7 +105,7 @@ int mla_decode_paged(const void* q, const void* kv_cache, int cache_dtype, const
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-int mla_decode_combine(const float* o_partial, const float* lse_partial, const int32_t* seq_lens,
+int mla_decode_combine(const void* o_partial, const float* lse_partial, const int32_t* seq_lens,
                        int B, int n_q, int H, int max_blocks, int pages_per_split, int max_splits,
                        void* out, float* lse, void* stream) {
   if (bad_stream_free_shape(B, n_q, H)) return MLA_ERR_BAD_SHAPE;
@@ -114,7 +114,7 @@ int mla_decode_combine(const float* o_partial, const float* lse_partial, const i
   if (B == 0) return MLA_OK;
   if (!o_partial || !lse_partial || !seq_lens || !out || !lse) return MLA_ERR_NULL_PTR;
   mla::CombineArgs a;
-  a.o_part = o_partial;
+  a.o_part = static_cast<const uint16_t*>(o_partial);
   a.lse_part = lse_partial;
   a.seq_lens = seq_lens;
   a.out = static_cast<uint16_t*>(out);

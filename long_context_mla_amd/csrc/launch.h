@@ -22,7 +22,7 @@ struct DecodeArgs {
   const float* kv_scale;
   const int32_t* block_table;
   const int32_t* seq_lens;
-  float* o_part;            // fp32 [B, max_splits, R, 512]
+  uint16_t* o_part;         // bf16 [B, max_splits, R, 512]
   float* lse_part;          // fp32 [B, max_splits, R]
   uint16_t* out;            // bf16 [B, R, 512]
   float* lse;               // fp32 [B, R]
@@ -31,7 +31,7 @@ struct DecodeArgs {
 };
 
 struct CombineArgs {
-  const float* o_part;
+  const uint16_t* o_part;   // bf16 [B, max_splits, R, 512]
   const float* lse_part;
   const int32_t* seq_lens;
   uint16_t* out;

@@ -14,6 +14,12 @@ namespace mla {
 
 constexpr int kWeightChunk = 1024;  // split weights held in LDS at a time
 
+// Four consecutive bf16 partial values (8 bytes) as floats (exact).
+__device__ __forceinline__ f32x4 load_bf16x4(const uint16_t* p) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  return f32x4{float_of(w.x << 16), float_of(w.x & 0xffff0000u), float_of(w.y << 16), float_of(w.y & 0xffff0000u)};
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int chunk = blockIdx.x & 3;
   const int br = blockIdx.x >> 2;  // b * R + r
@@ -31,7 +37,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int n_pages = (L + kPage - 1) / kPage;
   const int n_b = min(a.max_splits, (n_pages + a.pps - 1) / a.pps);
   const float* lse_b = a.lse_part + (int64_t)b * a.max_splits * a.R + r;
-  const float* o_b = a.o_part + ((int64_t)b * a.max_splits * a.R + r) * kDV + chunk * 128 + c4 * 4;
+  const uint16_t* o_b = a.o_part + ((int64_t)b * a.max_splits * a.R + r) * kDV + chunk * 128 + c4 * 4;
   const int64_t o_stride = (int64_t)a.R * kDV;
 
   float M = -INFINITY;
@@ -53,17 +59,17 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     __syncthreads();
     int s = s0 + g;
     for (; s + 24 < s1; s += 32) {
-      const f32x4 o0 = *reinterpret_cast<const f32x4*>(o_b + s * o_stride);
-      const f32x4 o1 = *reinterpret_cast<const f32x4*>(o_b + (s + 8) * o_stride);
-      const f32x4 o2 = *reinterpret_cast<const f32x4*>(o_b + (s + 16) * o_stride);
-      const f32x4 o3 = *reinterpret_cast<const f32x4*>(o_b + (s + 24) * o_stride);
+      const f32x4 o0 = load_bf16x4(o_b + s * o_stride);
+      const f32x4 o1 = load_bf16x4(o_b + (s + 8) * o_stride);
+      const f32x4 o2 = load_bf16x4(o_b + (s + 16) * o_stride);
+      const f32x4 o3 = load_bf16x4(o_b + (s + 24) * o_stride);
       const float w0 = s_w[s - s0], w1 = s_w[s + 8 - s0], w2 = s_w[s + 16 - s0], w3 = s_w[s + 24 - s0];
       acc += w0 * o0 + w1 * o1 + w2 * o2 + w3 * o3;
       wsum += (w0 + w1) + (w2 + w3);
     }
     for (; s < s1; s += 8) {
       const float w = s_w[s - s0];
-      acc += w * *reinterpret_cast<const f32x4*>(o_b + s * o_stride);
+      acc += w * load_bf16x4(o_b + s * o_stride);
       wsum += w;
     }
   }

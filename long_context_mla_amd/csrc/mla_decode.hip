@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
         if (a.max_splits == 1)
           a.out[((int64_t)b * a.R + r) * kDV + e % kDV] = 0;
         else
-          a.o_part[((int64_t)b * a.max_splits * a.R + r) * kDV + e % kDV] = 0.0f;
+          a.o_part[((int64_t)b * a.max_splits * a.R + r) * kDV + e % kDV] = 0;
       }
       for (int r = r0 + threadIdx.x; r < min(r0 + kRows, a.R); r += 256) {
         if (a.max_splits == 1)
@@ -510,118 +510,41 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
     prologue();
   };
 
-  if constexpr (T::PIPE) {
-    // Wait for this wave's own share of page it (the K rows of its 16 tokens),
-    // zero its rows past the end of the request (they may hold anything, even
-    // NaN codes, and P V multiplies them by zero weights), and read its K bytes.
-    auto k_read = [&](int it) {
-      if (it + 1 < n_it)
-        wait_vmcnt<LPP>();
-      else
-        wait_vmcnt<0>();
-      uint8_t* kv = s_kv[it % T::NBUF];
-      const int nvalid = L - (p_begin + it) * kPage;
-      if (nvalid < wave * 16 + 16) {
-        const int t0 = max(nvalid, wave * 16);
-        u32x4* junk = reinterpret_cast<u32x4*>(kv + t0 * T::ROW_BYTES);
-        for (int e = lane; e < (wave * 16 + 16 - t0) * (T::ROW_BYTES / 16); e += 64)
-          junk[e] = u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int i = 0; i < KB / 2; ++i) kraw[i] = *reinterpret_cast<const u32x4*>(kv + klane + 64 * i);
-    };
-    // Iteration it: after the barrier, the LDS reads of P V of page it - 1 are
-    // issued first; the scores of page it (K already in registers) cover their
-    // latency; then P V of page it - 1, the K reads of page it + 1 and the
-    // softmax weights of page it.  The first page is peeled off so that the
-    // steady-state loop is a single path; a restart (rare) repeats the split.
-    for (;;) {
-      k_read(0);
-      {
-        const bool next = T::DIST < n_it;
-        if (next) {
-          dma_page(T::DIST);
-          dma_part(0);
-          dma_part(1);
-        }
-        f32x4 S[2];
-        qk_fp8(S);
-        if (1 < n_it) k_read(1);
-        scores(S, 0);
-        if (!have_ref) first_ref();
-        weights(0);
-        if (next) dma_part(2);
-      }
-      bool again = false;
-      for (int it = 1; it < n_it; ++it) {
-        __syncthreads();  // P, flags and every wave's share of page it - 1 are in LDS;
-                          // every wave is done with page it - 2 and P of it - 2
-        const int4 fl = *reinterpret_cast<const int4*>(&s_flag[(it - 1) & 1][0]);
-        pv_read(s_kv[(it - 1) % T::NBUF], s_p[(it - 1) & 1]);
-        const bool next = it + T::DIST < n_it;
-        if (next) {
-          dma_page(it + T::DIST);
-          dma_part(0);
-        }
-        f32x4 S[2];
-        qk_fp8(S);
-        if ((fl.x | fl.y | fl.z | fl.w) && restarts < kMaxRestarts) {
-          again = true;
-          break;
-        }
-        pv_math([&] { if (next) dma_part(1); });
-        if (it + 1 < n_it) k_read(it + 1);
-        scores(S, it);
-        weights(it);
-        if (next) dma_part(2);
-      }
-      if (!again) {
-        __syncthreads();  // P and flags of the last page are in LDS
-        if (flagged(n_it - 1)) {
-          again = true;
-        } else {
-          pv_read(s_kv[(n_it - 1) % T::NBUF], s_p[(n_it - 1) & 1]);
-          pv_math(no_mid);
-        }
-      }
-      if (!again) break;
+  static_assert(!T::PIPE, "this kernel serves the BF16 cache; FP8 has its own");
+  for (int it = 0; it < n_it; ++it) {
+    wait_vmcnt<0>();
+    __syncthreads();  // page it is in LDS; every wave is done with page it - 1
+    const bool next = it + T::DIST < n_it;
+    if (next) {
+      dma_page(it + T::DIST);
+      dma_part(0);
+      dma_part(1);
+      dma_part(2);
+    }
+    uint8_t* kv = s_kv[it % T::NBUF];
+    const int nvalid = min(kPage, L - (p_begin + it) * kPage);
+    if (nvalid < kPage) {
+      // rows past the end of the request may hold anything (even NaN codes):
+      // zero them so that their zero weights give zero products in PV
+      u32x4* junk = reinterpret_cast<u32x4*>(kv + nvalid * T::ROW_BYTES);
+      for (int e = threadIdx.x; e < (kPage - nvalid) * (T::ROW_BYTES / 16); e += 256)
+        junk[e] = u32x4{0u, 0u, 0u, 0u};
+    }
+    f32x4 S[2];
+    qk_bf16(kv, S);
+    mfma_result_fence_v(S[0], S[1]);
+    scores(S, it);
+    if (!have_ref) first_ref();
+    weights(it);
+    __syncthreads();  // P of the page is in LDS
+    if (flagged(it)) {
       restart();
+      it = -1;
+      continue;
     }
-  } else {
-    for (int it = 0; it < n_it; ++it) {
-      wait_vmcnt<0>();
-      __syncthreads();  // page it is in LDS; every wave is done with page it - 1
-      const bool next = it + T::DIST < n_it;
-      if (next) {
-        dma_page(it + T::DIST);
-        dma_part(0);
-        dma_part(1);
-        dma_part(2);
-      }
-      uint8_t* kv = s_kv[it % T::NBUF];
-      const int nvalid = min(kPage, L - (p_begin + it) * kPage);
-      if (nvalid < kPage) {
-        // rows past the end of the request may hold anything (even NaN codes):
-        // zero them so that their zero weights give zero products in PV
-        u32x4* junk = reinterpret_cast<u32x4*>(kv + nvalid * T::ROW_BYTES);
-        for (int e = threadIdx.x; e < (kPage - nvalid) * (T::ROW_BYTES / 16); e += 256)
-          junk[e] = u32x4{0u, 0u, 0u, 0u};
-      }
-      f32x4 S[2];
-      qk_bf16(kv, S);
-      mfma_result_fence_v(S[0], S[1]);
-      scores(S, it);
-      if (!have_ref) first_ref();
-      weights(it);
-      __syncthreads();  // P of the page is in LDS
-      if (flagged(it)) {
-        restart();
-        it = -1;
-        continue;
-      }
-      pv(kv, s_p[it & 1], no_mid);
-    }
+    pv(kv, s_p[it & 1], no_mid);
   }
+
 
   // ---- epilogue: softmax sums across lanes and token groups, then O / l
   mfma_result_fence_v16(O);
@@ -659,9 +582,9 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
         if (wave == 0 && m == 0) a.lse[(int64_t)b * a.R + r] = lse_nat;
       } else {
         const int64_t pr = ((int64_t)b * a.max_splits + split) * a.R + r;
-        float* dst = a.o_part + pr * kDV + dim0 + m;
+        uint16_t* dst = a.o_part + pr * kDV + dim0 + m;
 #pragma unroll
-        for (int db = 0; db < 8; ++db) dst[db * 16] = O[rbp][db][i] * inv;
+        for (int db = 0; db < 8; ++db) dst[db * 16] = float_to_bf16(O[rbp][db][i] * inv);
         if (wave == 0 && m == 0) a.lse_part[pr] = lse_nat;
       }
     }

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
         if (a.max_splits == 1)
           a.out[((int64_t)b * a.R + r) * kDV + e % kDV] = 0;
         else
-          a.o_part[((int64_t)b * a.max_splits * a.R + r) * kDV + e % kDV] = 0.0f;
+          a.o_part[((int64_t)b * a.max_splits * a.R + r) * kDV + e % kDV] = 0;
       }
       for (int r = r0 + threadIdx.x; r < min(r0 + kRows, a.R); r += 512) {
         if (a.max_splits == 1)
@@ -209,10 +209,17 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
 
     // Wait for this wave's own share of page it, zero its rows past the end of
     // the request (they may hold anything, even NaN codes, and P V multiplies
-    // them by zero weights), and read its K bytes.
-    auto k_read = [&](int it) {
-      if (it + 1 < n_it)
+    // them by zero weights), and read its K bytes.  Loads complete in order, so
+    // the wait allows exactly the loads issued after page it's: a whole page
+    // (LPP) right after the prologue, the scale and the first two parts of
+    // page it + 1 inside the loop (its third part is issued later), none at the
+    // end of the split.
+    constexpr int AHEAD = 2 * T::PART + (SCALE == kScaleToken ? 1 : 0);
+    auto k_read = [&](int it, int after) {
+      if (after == LPP)
         wait_vmcnt<LPP>();
+      else if (after == AHEAD)
+        wait_vmcnt<AHEAD>();
       else
         wait_vmcnt<0>();
       uint8_t* kv = s_kv[it % T::NBUF];
@@ -312,7 +319,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     };
 
     for (;;) {
-      k_read(0);
+      k_read(0, n_it > 1 ? LPP : 0);
       {
         // page 0 (the first page of an attempt)
         const bool next = T::DIST < n_it;
@@ -323,7 +330,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
         }
         f32x4 S[2];
         qk(S);
-        if (1 < n_it) k_read(1);
+        if (1 < n_it) k_read(1, next ? AHEAD : 0);
         scores(S, 0);
         if (!have_ref) {
           // the reference of each row is its maximum over the first page
@@ -358,7 +365,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
         f32x4 S[2];
         qk(S);
         if (next) dma_part(1);
-        if (it + 1 < n_it) k_read(it + 1);
+        if (it + 1 < n_it) k_read(it + 1, next ? AHEAD : 0);
         scores(S, it);
         weights(it);
         if (next) dma_part(2);
@@ -510,9 +517,9 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
           if (qw == 0 && m == 0) a.lse[(int64_t)b * a.R + r] = lse_nat;
         } else {
           const int64_t pr = ((int64_t)b * a.max_splits + split) * a.R + r;
-          float* dst = a.o_part + pr * kDV + dim0 + m;
+          uint16_t* dst = a.o_part + pr * kDV + dim0 + m;
 #pragma unroll
-          for (int db = 0; db < 8; ++db) dst[db * 16] = O[rbp][db][i] * inv;
+          for (int db = 0; db < 8; ++db) dst[db * 16] = float_to_bf16(O[rbp][db][i] * inv);
           if (qw == 0 && m == 0) a.lse_part[pr] = lse_nat;
         }
       }

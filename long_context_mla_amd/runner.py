@@ -21,7 +21,7 @@ class DecodeStep:
         self.lse = torch.empty((B, n_q, H), dtype=torch.float32, device=device)
         if self.max_splits > 1:
             self.o_partial = torch.empty((B, self.max_splits, n_q, H, _lib.VALUE_DIM),
-                                         dtype=torch.float32, device=device)
+                                         dtype=torch.bfloat16, device=device)
             self.lse_partial = torch.empty((B, self.max_splits, n_q, H), dtype=torch.float32,
                                            device=device)
         else:

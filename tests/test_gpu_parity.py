@@ -223,14 +223,16 @@ def test_combine_matches_oracle_merge():
     rng = np.random.default_rng(10)
     B, n_q, H, max_splits, pps, max_blocks = 3, 2, 16, 6, 2, 12
     seq = np.array([700, 64, 1], np.int32)  # 11, 1 and 1 pages -> 6, 1, 1 splits
-    o = rng.standard_normal((B, max_splits, n_q, H, 512)).astype(np.float32)
+    o_bits = synth.bf16_bits(rng.standard_normal((B, max_splits, n_q, H, 512)).astype(np.float32))
+    o = (o_bits.astype(np.uint32) << 16).view(np.float32)  # the bf16 partials, exactly
     ls = rng.uniform(-20, 20, (B, max_splits, n_q, H)).astype(np.float32)
     ls[0, 2, 0, :5] = -np.inf
     ls[1, 0, 1, 3] = -np.inf  # a row with no visible token at all
     d = torch.device("cuda:0")
     out = torch.empty((B, n_q, H, 512), dtype=torch.bfloat16, device=d)
     lse = torch.empty((B, n_q, H), dtype=torch.float32, device=d)
-    mla.mla_decode_combine(torch.from_numpy(o).to(d), torch.from_numpy(ls).to(d),
+    o_dev = torch.from_numpy(o_bits.view(np.int16)).view(torch.bfloat16).to(d)
+    mla.mla_decode_combine(o_dev, torch.from_numpy(ls).to(d),
                            torch.from_numpy(seq).to(d), max_blocks, pps, out, lse)
     torch.cuda.synchronize()
     got_o, got_l = bf16_tensor_to_f64(out), lse.cpu().double().numpy()
@@ -242,3 +244,22 @@ def test_combine_matches_oracle_merge():
         fin = np.isfinite(rl)
         assert np.array_equal(fin, np.isfinite(got_l[b]))
         assert np.max(np.abs(got_l[b][fin] - rl[fin])) <= 1e-5 * 40
+
+
+@pytest.mark.parametrize("scale_mode", ["token", "tensor"])
+def test_long_split_repeatable(scale_mode):
+    """One request of 188 pages decoded as one split and as two (both cross the
+    64-page boundaries of the page-id reads): three runs of each plan are
+    bitwise identical and match the oracle.  A page read before its copy has
+    landed shows up here as run-to-run differences."""
+    w = synth.custom(f"long_split_{scale_mode}", B=1, n_q=1, H=64, context_lens=(12000,),
+                     cache_dtype="fp8", scale_mode=scale_mode, seed=5)
+    g = GpuState(w)
+    ref_o, ref_l = oracle_decode(w)
+    g.step()  # appends the new row
+    npg = int(-(-w.seq_lens.max() // 64))
+    for pps, ms in [(npg, 1), (100, 2)]:
+        runs = [g.decode_only(pps, ms) for _ in range(3)]
+        for o, l in runs[1:]:
+            assert np.array_equal(o, runs[0][0]) and np.array_equal(l, runs[0][1]), f"pps={pps}"
+        compare(runs[0][0], runs[0][1], ref_o, ref_l, tag=f"long split pps={pps} splits={ms}")
