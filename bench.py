@@ -2,7 +2,10 @@
 """Benchmark one decode step of paged FP8 MLA attention on one MI355X.
 
 A step is the whole hot path on one batch: kv_append_fp8 of the step's new
-latent rows, split-KV mla_decode_paged, and mla_decode_combine.  The default
+latent rows, split-KV mla_decode_paged, and mla_decode_combine.  Steps are
+timed as replays of one HIP graph per step (a serving loop's form); the decode
+kernel's own duration comes from a separate eager pass with HIP events around
+every launch (--no-graph times eager steps only).  The default
 workload is one request of 64 heads over a 100,000-token FP8 e4m3 cache
 (+1 appended row) with a per-tensor scale, randomly permuted 64-token pages.
 
@@ -45,6 +48,8 @@ def parse():
     ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--max-splits", type=int, default=0)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of one HIP graph per step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes --steps times (the "
                          "reference reading for HBM traffic counters) and exit")
@@ -188,20 +193,23 @@ def main():
                           pages_per_split=pps, max_splits=ms)
     stream = torch.cuda.current_stream()
 
-    def run(i, ev=None):
+    def run(i, ev=None, st=None):
+        st = st or stream
         k = i % args.rotate
         if new_rows is not None:
-            mla.kv_append_fp8(new_rows, caches[k], scales[k], w.scale_mode, bt, sl, stream=stream)
+            mla.kv_append_fp8(new_rows, caches[k], scales[k], w.scale_mode, bt, sl, stream=st)
         if ev is not None:
-            ev[0].record(stream)
-        step.decode(q, caches[k], scales[k], w.scale_mode, bt, sl, w.softmax_scale, stream=stream)
+            ev[0].record(st)
+        step.decode(q, caches[k], scales[k], w.scale_mode, bt, sl, w.softmax_scale, stream=st)
         if ev is not None:
-            ev[1].record(stream)
-        step.combine(sl, stream=stream)
+            ev[1].record(st)
+        step.combine(sl, stream=st)
 
     for i in range(args.warmup):
         run(i)
     torch.cuda.synchronize()
+    # Pass 1, eager launches: HIP events around every decode launch on its
+    # stream give the decode kernel's duration (the roofline figure).
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -211,9 +219,32 @@ def main():
         run(args.warmup + i, evs[i])
     end.record(stream)
     torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / args.steps
+    ms_step_eager = start.elapsed_time(end) / args.steps
     k_ms = np.array([a.elapsed_time(b) for a, b in evs])
     k_us = float(k_ms.mean() * 1000)
+    ms_step = ms_step_eager
+    if not args.no_graph:
+        # Pass 2: each step (append, decode, combine) as one HIP graph per
+        # rotated cache, replayed back to back as a serving loop would.
+        graphs = []
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            for k in range(args.rotate):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    run(k, st=cap)
+                graphs.append(g)
+        stream.wait_stream(cap)
+        for i in range(args.warmup):
+            graphs[i % args.rotate].replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            graphs[(args.warmup + i) % args.rotate].replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms_step = start.elapsed_time(end) / args.steps
 
     tokens = w.total_tokens()
     unique = w.unique_tokens()
@@ -266,6 +297,8 @@ def main():
         "hbm_tb_s_step": round(alg_bytes / (ms_step * 1e-3) / 1e12, 3),
         "roofline_frac_step": round(max(t_hbm, t_mfma) / (ms_step * 1e-3), 4),
         "decode_kernel_us_p10_p50_p90": [round(float(np.percentile(k_ms, p)) * 1000, 2) for p in (10, 50, 90)],
+        "step_launch": "eager" if args.no_graph else "hip graph per step",
+        "ms_per_step_eager": round(ms_step_eager, 5),
         "setup_s": round(t_setup, 1),
     }
     if not args.no_cpu_baseline:
