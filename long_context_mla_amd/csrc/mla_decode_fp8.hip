@@ -46,6 +46,9 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   __shared__ float s_m0[kRows];
   __shared__ __attribute__((aligned(16))) int s_flag[2][4];
 
+  // One round trip for the launch arguments the first loads need: without
+  // this the compiler fetches them in dependent batches.
+  asm volatile("" :: "s"(a.q), "s"(a.block_table), "s"(a.seq_lens), "s"(a.n_rg), "s"(a.max_blocks));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool scorer = wave < 4;
@@ -59,14 +62,42 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   const int rg = kx % a.n_rg;
   const int split = (kx / a.n_rg) * 8 + xcd;
   if (split >= a.max_splits) return;
-  const int L = min(max(load_const(a.seq_lens, b), 0), a.max_blocks * kPage);
-  const int n_pages = (L + kPage - 1) / kPage;
   const int r0 = rg * kRows;
   const int p_begin = split * a.pps;
+  const int64_t bt_row = (int64_t)b * a.max_blocks;
+  constexpr int QBUF = T::NBUF - 1;
+
+  // Before anything waits, the score waves issue the two loads that depend on
+  // the launch arguments alone, so that their latencies overlap the length's:
+  //  * the split's first 64 page ids (bounded by the table row, not yet by the
+  //    length), one per lane;
+  //  * the query of the group's 32 rows, HBM -> LDS in one coalesced copy
+  //    shared by the four score waves, into the page buffer that stays free
+  //    until the third page copy.  Row r's 16-byte chunk c (72 per row) goes to
+  //    slot r * 72 + (c ^ ((r / 2) % 8)), which makes the operand reads below
+  //    free of bank conflicts.  Rows past R repeat row R - 1 (results dropped).
+  int ids = 0;
+  if (scorer) {
+    const int idx = p_begin + lane;
+    if (idx < a.max_blocks) ids = a.block_table[bt_row + idx];
+    const uint16_t* qbase = a.q + ((int64_t)b * a.R + r0) * kD;
+    const int rmax = a.R - 1 - r0;
+    const uint32_t qlds = lds_addr(&s_kv[QBUF][0]);
+#pragma unroll
+    for (int j = 0; j < 9; ++j) {
+      const int slot = (qw * 9 + j) * 64 + lane;  // 2304 slots = 32 rows x 72 chunks
+      const int r = slot / 72;
+      const int c = (slot - r * 72) ^ ((r >> 1) & 7);
+      lds_dma16(qbase, (uint32_t)(min(r, rmax) * (kD * 2) + c * 16), qlds + (qw * 9 + j) * 1024);
+    }
+  }
+  const int L = min(max(load_const(a.seq_lens, b), 0), a.max_blocks * kPage);
+  const int n_pages = (L + kPage - 1) / kPage;
 
   if (p_begin >= n_pages) {
     // Nothing to read.  Only an empty request's first split reports it; the
     // combine never reads splits past a request's last page.
+    if (scorer) wait_vmcnt<0>();  // the query copy lands before the workgroup ends
     if (n_pages == 0 && split == 0) {
       for (int e = threadIdx.x; e < kRows * kDV; e += 512) {
         const int r = r0 + e / kDV;
@@ -100,32 +131,14 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     // score waves
     // =====================================================================
     const float coef = a.sm_log2 * tscale;
-    constexpr int QBUF = T::NBUF - 1;
-    // The query of the group's 32 rows, HBM -> LDS in one coalesced copy
-    // shared by the four score waves, into the page buffer that stays free
-    // until the third page copy.  Row r's 16-byte chunk c (72 per row) goes to
-    // slot r * 72 + (c ^ ((r / 2) % 8)), which makes the operand reads below
-    // free of bank conflicts.  Rows past R repeat row R - 1 (results dropped).
-    const uint32_t qlds = lds_addr(&s_kv[QBUF][0]);
-#pragma unroll
-    for (int j = 0; j < 9; ++j) {
-      const int slot = (qw * 9 + j) * 64 + lane;  // 2304 slots = 32 rows x 72 chunks
-      const int r = slot / 72;
-      const int c = (slot - r * 72) ^ ((r >> 1) & 7);
-      const uint16_t* src = a.q + ((int64_t)b * a.R + min(r0 + r, a.R - 1)) * kD + c * 8;
-      lds_dma16_lane(src, qlds + (qw * 9 + j) * 1024);
-    }
-
     // Page ids of the split, 64 at a time, one per lane; picked out with
-    // readlane so the DMA issue never waits on a scalar load.
-    const int64_t bt_row = (int64_t)b * a.max_blocks;
+    // readlane so the DMA issue never waits on a scalar load.  Ids past the
+    // split are never used; every used one is clamped to the pool.
     auto load_ids = [&](int first) {
       const int idx = first + lane;
-      int pg = idx < p_end ? a.block_table[bt_row + idx] : 0;
-      return min(max(pg, 0), a.num_pages - 1);
+      return idx < p_end ? a.block_table[bt_row + idx] : 0;
     };
     int id_chunk = 0;
-    int ids = load_ids(p_begin);
 
     // causal limit of this lane's rows rb*16 + m: row i*H + h sees tokens
     // t < L - n_q + i + 1; lim_lo is the first token any real row of the group
@@ -148,33 +161,26 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
       const int t = slot / Z::NCH;
       goff[j] = t * T::ROW_BYTES + Z::chunk_of_slot(t, slot - t * Z::NCH) * 16;
     }
-    const uint8_t* dma_src = a.cache;
-    uint32_t dma_dst = 0;
-    auto dma_page = [&](int it) {  // select page p_begin + it for the following dma_part calls
+    // Page p_begin + it (and its scales) HBM -> its LDS buffer.  The whole
+    // copy is issued at once, two pages ahead of its use, which leaves it about
+    // one and a half page times to land.
+    auto dma_page = [&](int it) {
       if ((it >> 6) != id_chunk) {
         id_chunk = it >> 6;
         ids = load_ids(p_begin + (id_chunk << 6));
       }
-      const int pg = __builtin_amdgcn_readlane(ids, it & 63);
-      dma_src = a.cache + (int64_t)pg * T::PAGE_BYTES;
-      dma_dst = lds_addr(&s_kv[it % T::NBUF][0]) + qw * T::LOADS * 1024;
+      const int pg = min(max(__builtin_amdgcn_readlane(ids, it & 63), 0), a.num_pages - 1);
+      const uint8_t* src = a.cache + (int64_t)pg * T::PAGE_BYTES;
+      const uint32_t dst = lds_addr(&s_kv[it % T::NBUF][0]) + qw * T::LOADS * 1024;
       if (SCALE == kScaleToken)
         lds_dma4(a.kv_scale + (int64_t)pg * kPage, lane * 4, lds_addr(&s_scale[it % T::NBUF][0]));
-    };
-    auto dma_part = [&](int part) {
 #pragma unroll
-      for (int j = 0; j < T::LOADS; ++j)
-        if (j / T::PART == part) lds_dma16(dma_src, goff[j], dma_dst + j * 1024);
+      for (int j = 0; j < T::LOADS; ++j) lds_dma16(src, goff[j], dst + j * 1024);
     };
     auto prologue = [&]() {
 #pragma unroll
       for (int k = 0; k < T::DIST; ++k)
-        if (k < n_it) {
-          dma_page(k);
-          dma_part(0);
-          dma_part(1);
-          dma_part(2);
-        }
+        if (k < n_it) dma_page(k);
     };
     prologue();
 
@@ -210,16 +216,11 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     // Wait for this wave's own share of page it, zero its rows past the end of
     // the request (they may hold anything, even NaN codes, and P V multiplies
     // them by zero weights), and read its K bytes.  Loads complete in order, so
-    // the wait allows exactly the loads issued after page it's: a whole page
-    // (LPP) right after the prologue, the scale and the first two parts of
-    // page it + 1 inside the loop (its third part is issued later), none at the
-    // end of the split.
-    constexpr int AHEAD = 2 * T::PART + (SCALE == kScaleToken ? 1 : 0);
-    auto k_read = [&](int it, int after) {
-      if (after == LPP)
+    // the wait allows exactly the loads issued after page it's: the whole next
+    // page (LPP) when one is in flight behind it, none at the end of the split.
+    auto k_read = [&](int it, bool page_behind) {
+      if (page_behind)
         wait_vmcnt<LPP>();
-      else if (after == AHEAD)
-        wait_vmcnt<AHEAD>();
       else
         wait_vmcnt<0>();
       uint8_t* kv = s_kv[it % T::NBUF];
@@ -319,18 +320,16 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     };
 
     for (;;) {
-      k_read(0, n_it > 1 ? LPP : 0);
+      k_read(0, n_it > 1);
       {
         // page 0 (the first page of an attempt)
         const bool next = T::DIST < n_it;
         if (next) {
           dma_page(T::DIST);
-          dma_part(0);
-          dma_part(1);
         }
         f32x4 S[2];
         qk(S);
-        if (1 < n_it) k_read(1, next ? AHEAD : 0);
+        if (1 < n_it) k_read(1, next);
         scores(S, 0);
         if (!have_ref) {
           // the reference of each row is its maximum over the first page
@@ -352,7 +351,6 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
           have_ref = true;
         }
         weights(0);
-        if (next) dma_part(2);
       }
       __syncthreads();  // (3) P and flags of page 0 are in LDS
       bool again = flagged(0);
@@ -360,15 +358,12 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
         const bool next = it + T::DIST < n_it;
         if (next) {
           dma_page(it + T::DIST);
-          dma_part(0);
         }
         f32x4 S[2];
         qk(S);
-        if (next) dma_part(1);
-        if (it + 1 < n_it) k_read(it + 1, next ? AHEAD : 0);
+        if (it + 1 < n_it) k_read(it + 1, next);
         scores(S, it);
         weights(it);
-        if (next) dma_part(2);
         __syncthreads();  // (4) P and flags of page it are in LDS; page it - 1 is consumed
         again = flagged(it);
       }
@@ -494,35 +489,47 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
       mfma_zero_o(O);
     }
 
-    __syncthreads();  // (6) the score waves' sums are in LDS
-    const int dim0 = qw * 128;
+    __syncthreads();  // (6) the score waves' sums are in LDS; every page buffer is free
+    // Row normalisation: lane r < 32 of each output wave computes row r's
+    // factor into this wave's slice of s_red (free by now); wave 4 also writes
+    // the row's LSE.  The output is a weighted mean with the bf16 weights P V
+    // used; the LSE uses the fp32 weights.
+    const bool single = a.max_splits == 1;
+    const int64_t prow0 = single ? (int64_t)b * a.R + r0 : ((int64_t)b * a.max_splits + split) * a.R + r0;
+    if (lane < kRows) {
+      const int row = lane;
+      const float lt = s_lsum[0][row] + s_lsum[1][row] + s_lsum[2][row] + s_lsum[3][row];
+      const float ln = s_lnrm[0][row] + s_lnrm[1][row] + s_lnrm[2][row] + s_lnrm[3][row];
+      s_red[qw][row] = ln > 0.0f ? tscale / ln : 0.0f;
+      if (qw == 0 && r0 + row < a.R) {
+        const float mr = s_m0[row] == -INFINITY ? 0.0f : s_m0[row];
+        (single ? a.lse : a.lse_part)[prow0 + row] = lt > 0.0f ? (mr + __log2f(lt)) * kLn2 : -INFINITY;
+      }
+    }
+    // O goes out through LDS so that each store moves 16 contiguous bytes:
+    // this wave's 32 x 128 fp32 tile, rows 132 floats apart (conflict-free
+    // writes of the MFMA layout), then 8 dims of one row per lane.  Only this
+    // wave touches its tile, and a wave's LDS accesses complete in order.
+    constexpr int SST = 132;
+    float* tile = reinterpret_cast<float*>(&s_kv[0][0]) + qw * (kRows * SST);
 #pragma unroll
     for (int rbp = 0; rbp < 2; ++rbp)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = rbp * 16 + 4 * g + i;
-        const int r = r0 + row;
-        if (r >= a.R) continue;
-        const float lt = s_lsum[0][row] + s_lsum[1][row] + s_lsum[2][row] + s_lsum[3][row];
-        const float ln = s_lnrm[0][row] + s_lnrm[1][row] + s_lnrm[2][row] + s_lnrm[3][row];
-        // the output is a weighted mean with the bf16 weights PV used; the LSE
-        // uses the fp32 weights
-        const float inv = ln > 0.0f ? tscale / ln : 0.0f;
-        const float mr = s_m0[row] == -INFINITY ? 0.0f : s_m0[row];
-        const float lse_nat = lt > 0.0f ? (mr + __log2f(lt)) * kLn2 : -INFINITY;
-        if (a.max_splits == 1) {
-          uint16_t* dst = a.out + ((int64_t)b * a.R + r) * kDV + dim0 + m;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int db = 0; db < 8; ++db) dst[db * 16] = float_to_bf16(O[rbp][db][i] * inv);
-          if (qw == 0 && m == 0) a.lse[(int64_t)b * a.R + r] = lse_nat;
-        } else {
-          const int64_t pr = ((int64_t)b * a.max_splits + split) * a.R + r;
-          uint16_t* dst = a.o_part + pr * kDV + dim0 + m;
+        for (int db = 0; db < 8; ++db) tile[(rbp * 16 + 4 * g + i) * SST + 16 * db + m] = O[rbp][db][i];
+    uint16_t* dst = (single ? a.out : a.o_part) + prow0 * kDV + qw * 128;
 #pragma unroll
-          for (int db = 0; db < 8; ++db) dst[db * 16] = float_to_bf16(O[rbp][db][i] * inv);
-          if (qw == 0 && m == 0) a.lse_part[pr] = lse_nat;
-        }
-      }
+    for (int k = 0; k < 8; ++k) {
+      const int row = k * 4 + (lane >> 4), c = lane & 15;  // 32 rows x 16 chunks of 8 dims
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(&tile[row * SST + 8 * c]);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(&tile[row * SST + 8 * c + 4]);
+      const float inv = s_red[qw][row];
+      if (r0 + row < a.R)
+        *reinterpret_cast<u32x4*>(dst + (int64_t)row * kDV + 8 * c) =
+            u32x4{pack_bf16x2(v0.x * inv, v0.y * inv), pack_bf16x2(v0.z * inv, v0.w * inv),
+                  pack_bf16x2(v1.x * inv, v1.y * inv), pack_bf16x2(v1.z * inv, v1.w * inv)};
+    }
   }
 }
 
