@@ -76,10 +76,13 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   //    until the third page copy.  Row r's 16-byte chunk c (72 per row) goes to
   //    slot r * 72 + (c ^ ((r / 2) % 8)), which makes the operand reads below
   //    free of bank conflicts.  Rows past R repeat row R - 1 (results dropped).
+  // Every load of page ids is inline asm, awaited explicitly with the result
+  // tied to the wait: a load the compiler tracks would make it wait for all
+  // copies in flight before each later readlane of the ids.
   int ids = 0;
   if (scorer) {
-    const int idx = p_begin + lane;
-    if (idx < a.max_blocks) ids = a.block_table[bt_row + idx];
+    const int32_t* id_src = a.block_table + bt_row + min(p_begin + lane, a.max_blocks - 1);
+    asm volatile("global_load_dword %0, %1, off" : "=v"(ids) : "v"(id_src) : "memory");
     const uint16_t* qbase = a.q + ((int64_t)b * a.R + r0) * kD;
     const int rmax = a.R - 1 - r0;
     const uint32_t qlds = lds_addr(&s_kv[QBUF][0]);
@@ -133,12 +136,16 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     const float coef = a.sm_log2 * tscale;
     // Page ids of the split, 64 at a time, one per lane; picked out with
     // readlane so the DMA issue never waits on a scalar load.  Ids past the
-    // split are never used; every used one is clamped to the pool.
-    auto load_ids = [&](int first) {
-      const int idx = first + lane;
-      return idx < p_end ? a.block_table[bt_row + idx] : 0;
-    };
+    // split are never used; every used one is clamped to the pool.  The first
+    // chunk was requested at the start (it lands with the query copy); later
+    // chunks, and the first again on a restart, wait for themselves.
+    asm volatile("s_waitcnt vmcnt(0)" : "+v"(ids) :: "memory");
     int id_chunk = 0;
+    auto reload_ids = [&](int chunk) {
+      id_chunk = chunk;
+      const int32_t* src = a.block_table + bt_row + min(p_begin + (chunk << 6) + lane, p_end - 1);
+      asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(ids) : "v"(src) : "memory");
+    };
 
     // causal limit of this lane's rows rb*16 + m: row i*H + h sees tokens
     // t < L - n_q + i + 1; lim_lo is the first token any real row of the group
@@ -161,26 +168,30 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
       const int t = slot / Z::NCH;
       goff[j] = t * T::ROW_BYTES + Z::chunk_of_slot(t, slot - t * Z::NCH) * 16;
     }
-    // Page p_begin + it (and its scales) HBM -> its LDS buffer.  The whole
-    // copy is issued at once, two pages ahead of its use, which leaves it about
-    // one and a half page times to land.
+    // Page p_begin + it (and its scales) HBM -> its LDS buffer, two pages
+    // ahead of its use.  dma_page picks the page and copies the scales;
+    // dma_load(j) issues this wave's j-th 16-byte load of it.  Inside the loop
+    // the nine loads ride between the QK^T MFMAs: issued in one burst, the four
+    // score waves' 36 loads back up the CU's address path and stall the wave.
+    const uint8_t* dma_src = a.cache;
+    uint32_t dma_dst = 0;
     auto dma_page = [&](int it) {
-      if ((it >> 6) != id_chunk) {
-        id_chunk = it >> 6;
-        ids = load_ids(p_begin + (id_chunk << 6));
-      }
+      if ((it >> 6) != id_chunk) reload_ids(it >> 6);
       const int pg = min(max(__builtin_amdgcn_readlane(ids, it & 63), 0), a.num_pages - 1);
-      const uint8_t* src = a.cache + (int64_t)pg * T::PAGE_BYTES;
-      const uint32_t dst = lds_addr(&s_kv[it % T::NBUF][0]) + qw * T::LOADS * 1024;
+      dma_src = a.cache + (int64_t)pg * T::PAGE_BYTES;
+      dma_dst = lds_addr(&s_kv[it % T::NBUF][0]) + qw * T::LOADS * 1024;
       if (SCALE == kScaleToken)
         lds_dma4(a.kv_scale + (int64_t)pg * kPage, lane * 4, lds_addr(&s_scale[it % T::NBUF][0]));
-#pragma unroll
-      for (int j = 0; j < T::LOADS; ++j) lds_dma16(src, goff[j], dst + j * 1024);
     };
+    auto dma_load = [&](int j) { lds_dma16(dma_src, goff[j], dma_dst + j * 1024); };
     auto prologue = [&]() {
 #pragma unroll
       for (int k = 0; k < T::DIST; ++k)
-        if (k < n_it) dma_page(k);
+        if (k < n_it) {
+          dma_page(k);
+#pragma unroll
+          for (int j = 0; j < T::LOADS; ++j) dma_load(j);
+        }
     };
     prologue();
 
@@ -236,7 +247,8 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     };
     // S^T[token][row] = K Q^T for this wave's 16 tokens, all 32 rows: one MFMA
     // pair per k-block with the conversions of the next k-block between them.
-    auto qk = [&](f32x4 (&S)[2]) {
+    static_assert(T::LOADS * 2 == kD / 32, "one page load per two k-blocks");
+    auto qk = [&](f32x4 (&S)[2], bool dma) {
       auto lo_word = [&](int kb) { const u32x4 w = kraw[kb >> 1]; return (kb & 1) ? w[2] : w[0]; };
       auto hi_word = [&](int kb) { const u32x4 w = kraw[kb >> 1]; return (kb & 1) ? w[3] : w[1]; };
       uint32_t d[2][4];
@@ -249,6 +261,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
         const bf16x8 kop = bf16x8_of(d[kb & 1]);
         uint32_t (&nx)[4] = d[(kb + 1) & 1];
         if (kb == 0) mfma_vvv0_w(S[0], kop, qop[0][0]); else mfma_vvv_w(S[0], kop, qop[0][kb]);
+        if (dma && (kb & 1) == 0) dma_load(kb >> 1);
         if (kb + 1 < KB) {
           nx[0] = cvt_e4m3_lo(lo_word(kb + 1));
           nx[1] = cvt_e4m3_hi(lo_word(kb + 1));
@@ -324,11 +337,9 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
       {
         // page 0 (the first page of an attempt)
         const bool next = T::DIST < n_it;
-        if (next) {
-          dma_page(T::DIST);
-        }
+        if (next) dma_page(T::DIST);
         f32x4 S[2];
-        qk(S);
+        qk(S, next);
         if (1 < n_it) k_read(1, next);
         scores(S, 0);
         if (!have_ref) {
@@ -356,11 +367,9 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
       bool again = flagged(0);
       for (int it = 1; it < n_it && !again; ++it) {
         const bool next = it + T::DIST < n_it;
-        if (next) {
-          dma_page(it + T::DIST);
-        }
+        if (next) dma_page(it + T::DIST);
         f32x4 S[2];
-        qk(S);
+        qk(S, next);
         if (it + 1 < n_it) k_read(it + 1, next);
         scores(S, it);
         weights(it);
@@ -388,8 +397,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
         lsum[rb] = 0.0f;
         lnrm[rb] = 0.0f;
       }
-      id_chunk = 0;
-      ids = load_ids(p_begin);
+      reload_ids(0);
       prologue();
     }
     // the sums of this wave's tokens for the output waves
