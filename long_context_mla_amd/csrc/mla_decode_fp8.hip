@@ -26,6 +26,8 @@
 // weights 2^(y - m0); a weight above 2^64 restarts the split with a larger
 // reference (all waves together).  The output divides by the sum of the bf16
 // weights that P V used; the LSE uses the exact fp32 sum.
+#include <type_traits>
+
 #include "decode_tile.h"
 #include "device_common.h"
 #include "launch.h"
@@ -124,10 +126,11 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   const float tscale = SCALE == kScaleTensor ? load_const(a.kv_scale, 0) : 1.0f;
   bool have_ref = false;
   int restarts = 0;
-  auto flagged = [&](int it) {
+  auto flag_word = [&](int it) {
     const int4 f = *reinterpret_cast<const int4*>(&s_flag[it & 1][0]);
-    return (f.x | f.y | f.z | f.w) && restarts < kMaxRestarts;
+    return f.x | f.y | f.z | f.w;
   };
+  auto flagged = [&](int it) { return flag_word(it) && restarts < kMaxRestarts; };
 
   if (scorer) {
     // =====================================================================
@@ -248,7 +251,8 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     // S^T[token][row] = K Q^T for this wave's 16 tokens, all 32 rows: one MFMA
     // pair per k-block with the conversions of the next k-block between them.
     static_assert(T::LOADS * 2 == kD / 32, "one page load per two k-blocks");
-    auto qk = [&](f32x4 (&S)[2], bool dma) {
+    auto qk = [&](f32x4 (&S)[2], auto dma_c) {
+      constexpr bool dma = decltype(dma_c)::value;
       auto lo_word = [&](int kb) { const u32x4 w = kraw[kb >> 1]; return (kb & 1) ? w[2] : w[0]; };
       auto hi_word = [&](int kb) { const u32x4 w = kraw[kb >> 1]; return (kb & 1) ? w[3] : w[1]; };
       uint32_t d[2][4];
@@ -261,7 +265,9 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
         const bf16x8 kop = bf16x8_of(d[kb & 1]);
         uint32_t (&nx)[4] = d[(kb + 1) & 1];
         if (kb == 0) mfma_vvv0_w(S[0], kop, qop[0][0]); else mfma_vvv_w(S[0], kop, qop[0][kb]);
-        if (dma && (kb & 1) == 0) dma_load(kb >> 1);
+        if constexpr (dma) {
+          if ((kb & 1) == 0) dma_load(kb >> 1);
+        }
         if (kb + 1 < KB) {
           nx[0] = cvt_e4m3_lo(lo_word(kb + 1));
           nx[1] = cvt_e4m3_hi(lo_word(kb + 1));
@@ -337,9 +343,13 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
       {
         // page 0 (the first page of an attempt)
         const bool next = T::DIST < n_it;
-        if (next) dma_page(T::DIST);
         f32x4 S[2];
-        qk(S, next);
+        if (next) {
+          dma_page(T::DIST);
+          qk(S, std::true_type{});
+        } else {
+          qk(S, std::false_type{});
+        }
         if (1 < n_it) k_read(1, next);
         scores(S, 0);
         if (!have_ref) {
@@ -364,18 +374,31 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
         weights(0);
       }
       __syncthreads();  // (3) P and flags of page 0 are in LDS
-      bool again = flagged(0);
-      for (int it = 1; it < n_it && !again; ++it) {
-        const bool next = it + T::DIST < n_it;
-        if (next) dma_page(it + T::DIST);
+      // Page it's flags are read after the barrier that ends it but looked at
+      // only after the next page's QK^T MFMAs have been issued, so that the
+      // LDS latency of the read stays off the page's critical path.  On a
+      // restart that work (and a copy already issued) is simply dropped; the
+      // output waves leave their loop after the same barrier.
+      int fw = flag_word(0);
+      bool again = false;
+      auto page = [&](int it, auto dma_c) {  // false: leave for a restart
+        constexpr bool dma = decltype(dma_c)::value;
+        if constexpr (dma) dma_page(it + T::DIST);
         f32x4 S[2];
-        qk(S, next);
-        if (it + 1 < n_it) k_read(it + 1, next);
+        qk(S, dma_c);
+        if (fw && restarts < kMaxRestarts) return false;
+        if (it + 1 < n_it) k_read(it + 1, dma);
         scores(S, it);
         weights(it);
         __syncthreads();  // (4) P and flags of page it are in LDS; page it - 1 is consumed
-        again = flagged(it);
-      }
+        fw = flag_word(it);
+        return true;
+      };
+      int it = 1;
+      bool ok = true;
+      for (; ok && it + T::DIST < n_it; ++it) ok = page(it, std::true_type{});
+      for (; ok && it < n_it; ++it) ok = page(it, std::false_type{});
+      again = !ok || (fw && restarts < kMaxRestarts);
       if (!again) break;
       // A weight would exceed 2^64: restart the split with a reference raised
       // to each row's running maximum.
