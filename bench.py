@@ -1,8 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark one decode step of paged FP8 MLA attention on one MI355X.
 
-A step is the whole hot path on one batch: kv_append_fp8 of the step's new
-latent rows, split-KV mla_decode_paged, and mla_decode_combine.  Steps are
+A step is the whole hot path on one batch: the step's new latent rows go into
+the FP8 cache and the split-KV decode runs in one launch
+(mla_decode_paged_append: kv_append_fp8 + mla_decode_paged), then
+mla_decode_combine (--separate-append issues kv_append_fp8 on its own).  Steps are
 timed as replays of one HIP graph per step (a serving loop's form); the decode
 kernel's own duration comes from a separate eager pass with HIP events around
 every launch (--no-graph times eager steps only).  The default
@@ -48,6 +50,8 @@ def parse():
     ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--max-splits", type=int, default=0)
+    ap.add_argument("--separate-append", action="store_true",
+                    help="kv_append_fp8 as its own launch before mla_decode_paged")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of one HIP graph per step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -196,11 +200,17 @@ def main():
     def run(i, ev=None, st=None):
         st = st or stream
         k = i % args.rotate
-        if new_rows is not None:
+        fused = new_rows is not None and not args.separate_append
+        if new_rows is not None and not fused:
             mla.kv_append_fp8(new_rows, caches[k], scales[k], w.scale_mode, bt, sl, stream=st)
         if ev is not None:
             ev[0].record(st)
-        step.decode(q, caches[k], scales[k], w.scale_mode, bt, sl, w.softmax_scale, stream=st)
+        if fused:
+            mla.mla_decode_paged_append(new_rows, q, caches[k], scales[k], w.scale_mode, bt, sl,
+                                        w.softmax_scale, step.pps, step.max_splits, step.o_partial,
+                                        step.lse_partial, step.out, step.lse, stream=st)
+        else:
+            step.decode(q, caches[k], scales[k], w.scale_mode, bt, sl, w.softmax_scale, stream=st)
         if ev is not None:
             ev[1].record(st)
         step.combine(sl, stream=st)
@@ -298,6 +308,8 @@ def main():
         "roofline_frac_step": round(max(t_hbm, t_mfma) / (ms_step * 1e-3), 4),
         "decode_kernel_us_p10_p50_p90": [round(float(np.percentile(k_ms, p)) * 1000, 2) for p in (10, 50, 90)],
         "step_launch": "eager" if args.no_graph else "hip graph per step",
+        "append": "separate kv_append_fp8 launch" if args.separate_append or w.n_new == 0
+                  else "in the decode launch (mla_decode_paged_append)",
         "ms_per_step_eager": round(ms_step_eager, 5),
         "setup_s": round(t_setup, 1),
     }

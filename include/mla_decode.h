@@ -130,6 +130,34 @@ int mla_decode_paged(const void* q, const void* kv_cache, int cache_dtype, const
                      void* out, float* lse, void* stream);
 
 /*
+ * mla_decode_paged_append — kv_append_fp8 followed by mla_decode_paged on an
+ * FP8 cache, in one launch.  The new rows land in the cache's last page(s),
+ * which the decode reads in the same step; each workgroup that reads such a
+ * page encodes the rows itself (the same bytes kv_append_fp8 writes) and puts
+ * them over what its page copy brought, and one of them writes them, with
+ * their per-token scales, to the cache.  This saves the separate append
+ * launch and the wait between the two on every decode step.
+ *
+ *   kv_new, n_new   bf16 [B, n_new, 576] as in kv_append_fp8 (n_new = 0:
+ *                   plain decode); rows go to seq_lens[b] - n_new + j.
+ *   kv_cache        e4m3 codes [num_pages, 64, 576], written for the new rows.
+ *   kv_scale        PER_TOKEN: [num_pages, 64], written for the new rows;
+ *                   PER_TENSOR: [1], read.
+ *   the rest        as in mla_decode_paged (cache_dtype is MLA_CACHE_FP8_E4M3).
+ *
+ * After the call the cache and scales hold exactly what kv_append_fp8 would
+ * have written, and out / lse (or the partials) are bit-identical to those of
+ * mla_decode_paged on that cache.  A row whose position has no visible page
+ * (seq_lens[b] - n_new + j < 0) is skipped, as in kv_append_fp8.  Errors as in
+ * the two calls it replaces; MLA_ERR_UNSUPPORTED for MLA_SCALE_NONE.
+ */
+int mla_decode_paged_append(const void* kv_new, int n_new, const void* q, void* kv_cache,
+                            float* kv_scale, int scale_mode, const int32_t* block_table,
+                            const int32_t* seq_lens, int B, int n_q, int H, int max_blocks,
+                            int num_pages, float softmax_scale, int pages_per_split, int max_splits,
+                            void* o_partial, float* lse_partial, void* out, float* lse, void* stream);
+
+/*
  * mla_decode_combine — merge the split partials of mla_decode_paged
  * ("vLLM x AgentX", section "Model-specific parallelism / Kimi K3": partial
  * outputs and LSE statistics merged with online softmax).

@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     kv_append_fp8,
     mla_decode_combine,
     mla_decode_paged,
+    mla_decode_paged_append,
     mla_decode_plan,
     status_string,
 )

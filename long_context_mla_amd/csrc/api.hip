@@ -23,6 +23,56 @@ int check_cache_mode(int cache_dtype, int scale_mode) {
   return MLA_OK;
 }
 
+// The checks and the launch shared by mla_decode_paged and
+// mla_decode_paged_append (kv_new == nullptr, n_new == 0 for the former).
+int decode_impl(const void* q, const void* kv_cache, int cache_dtype, const float* kv_scale,
+                int scale_mode, const int32_t* block_table, const int32_t* seq_lens, int B, int n_q,
+                int H, int max_blocks, int num_pages, float softmax_scale, int pages_per_split,
+                int max_splits, void* o_partial, float* lse_partial, void* out, float* lse,
+                const void* kv_new, int n_new, void* stream) {
+  if (int s = check_cache_mode(cache_dtype, scale_mode)) return s;
+  if (bad_stream_free_shape(B, n_q, H)) return MLA_ERR_BAD_SHAPE;
+  if (max_blocks < 1 || num_pages < 1 || pages_per_split < 1 || max_splits < 1) return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)max_blocks * MLA_PAGE_SIZE > 2147483647LL) return MLA_ERR_BAD_SHAPE;
+  if (!std::isfinite(softmax_scale)) return MLA_ERR_BAD_SHAPE;
+  const int R = n_q * H;
+  const int rows = mla::decode_rows_per_group(B, R);
+  const int n_rg = (R + rows - 1) / rows;
+  if (((int64_t)max_splits + 7) / 8 * 8 * n_rg > kMaxGrid) return MLA_ERR_BAD_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!q || !kv_cache || !block_table || !seq_lens) return MLA_ERR_NULL_PTR;
+  if (scale_mode != MLA_SCALE_NONE && !kv_scale) return MLA_ERR_NULL_PTR;
+  if (max_splits == 1 && (!out || !lse)) return MLA_ERR_NULL_PTR;
+  if (max_splits > 1 && (!o_partial || !lse_partial)) return MLA_ERR_NULL_PTR;
+  mla::DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.cache = static_cast<const uint8_t*>(kv_cache);
+  a.kv_scale = kv_scale;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.o_part = static_cast<uint16_t*>(o_partial);
+  a.lse_part = lse_partial;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.B = B;
+  a.n_q = n_q;
+  a.H = H;
+  a.R = R;
+  a.max_blocks = max_blocks;
+  a.num_pages = num_pages;
+  a.pps = pages_per_split;
+  a.max_splits = max_splits;
+  a.n_rg = n_rg;
+  a.sm_log2 = softmax_scale * mla::kLog2e;
+  a.kv_new = static_cast<const uint16_t*>(kv_new);
+  a.n_new = n_new;
+  a.cache_out = static_cast<uint8_t*>(const_cast<void*>(kv_cache));
+  a.scale_out = const_cast<float*>(kv_scale);
+  const int kind = cache_dtype == MLA_CACHE_FP8_E4M3 ? mla::kFp8 : mla::kBf16;
+  const hipError_t e = mla::launch_decode(a, kind, scale_mode, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -66,43 +116,22 @@ int mla_decode_paged(const void* q, const void* kv_cache, int cache_dtype, const
                      int n_q, int H, int max_blocks, int num_pages, float softmax_scale,
                      int pages_per_split, int max_splits, void* o_partial, float* lse_partial,
                      void* out, float* lse, void* stream) {
-  if (int s = check_cache_mode(cache_dtype, scale_mode)) return s;
-  if (bad_stream_free_shape(B, n_q, H)) return MLA_ERR_BAD_SHAPE;
-  if (max_blocks < 1 || num_pages < 1 || pages_per_split < 1 || max_splits < 1) return MLA_ERR_BAD_SHAPE;
-  if ((int64_t)max_blocks * MLA_PAGE_SIZE > 2147483647LL) return MLA_ERR_BAD_SHAPE;
-  if (!std::isfinite(softmax_scale)) return MLA_ERR_BAD_SHAPE;
-  const int R = n_q * H;
-  const int rows = mla::decode_rows_per_group(B, R);
-  const int n_rg = (R + rows - 1) / rows;
-  if (((int64_t)max_splits + 7) / 8 * 8 * n_rg > kMaxGrid) return MLA_ERR_BAD_SHAPE;
-  if (B == 0) return MLA_OK;
-  if (!q || !kv_cache || !block_table || !seq_lens) return MLA_ERR_NULL_PTR;
-  if (scale_mode != MLA_SCALE_NONE && !kv_scale) return MLA_ERR_NULL_PTR;
-  if (max_splits == 1 && (!out || !lse)) return MLA_ERR_NULL_PTR;
-  if (max_splits > 1 && (!o_partial || !lse_partial)) return MLA_ERR_NULL_PTR;
-  mla::DecodeArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.cache = static_cast<const uint8_t*>(kv_cache);
-  a.kv_scale = kv_scale;
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
-  a.o_part = static_cast<uint16_t*>(o_partial);
-  a.lse_part = lse_partial;
-  a.out = static_cast<uint16_t*>(out);
-  a.lse = lse;
-  a.B = B;
-  a.n_q = n_q;
-  a.H = H;
-  a.R = R;
-  a.max_blocks = max_blocks;
-  a.num_pages = num_pages;
-  a.pps = pages_per_split;
-  a.max_splits = max_splits;
-  a.n_rg = n_rg;
-  a.sm_log2 = softmax_scale * mla::kLog2e;
-  const int kind = cache_dtype == MLA_CACHE_FP8_E4M3 ? mla::kFp8 : mla::kBf16;
-  const hipError_t e = mla::launch_decode(a, kind, scale_mode, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  return decode_impl(q, kv_cache, cache_dtype, kv_scale, scale_mode, block_table, seq_lens, B, n_q, H,
+                     max_blocks, num_pages, softmax_scale, pages_per_split, max_splits, o_partial,
+                     lse_partial, out, lse, nullptr, 0, stream);
+}
+
+int mla_decode_paged_append(const void* kv_new, int n_new, const void* q, void* kv_cache,
+                            float* kv_scale, int scale_mode, const int32_t* block_table,
+                            const int32_t* seq_lens, int B, int n_q, int H, int max_blocks,
+                            int num_pages, float softmax_scale, int pages_per_split, int max_splits,
+                            void* o_partial, float* lse_partial, void* out, float* lse, void* stream) {
+  if (scale_mode != MLA_SCALE_PER_TENSOR && scale_mode != MLA_SCALE_PER_TOKEN) return MLA_ERR_UNSUPPORTED;
+  if (n_new < 0) return MLA_ERR_BAD_SHAPE;
+  if (n_new > 0 && B > 0 && !kv_new) return MLA_ERR_NULL_PTR;
+  return decode_impl(q, kv_cache, MLA_CACHE_FP8_E4M3, kv_scale, scale_mode, block_table, seq_lens, B,
+                     n_q, H, max_blocks, num_pages, softmax_scale, pages_per_split, max_splits,
+                     o_partial, lse_partial, out, lse, n_new > 0 ? kv_new : nullptr, n_new, stream);
 }
 
 int mla_decode_combine(const void* o_partial, const float* lse_partial, const int32_t* seq_lens,

@@ -86,6 +86,50 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// One new latent row in E4M3, the encoding kv_append_fp8 defines: lane l takes
+// the 8-element chunks l and, for l < 8, l + 64 of the 576 bf16 values;
+// codes[c] holds chunk c's eight codes (element 0 in the low byte).  PER_TOKEN
+// (all 64 lanes take part): scale = amax / 448 (1 for an all-zero row);
+// otherwise the given tensor_scale.  Returns the scale.
+template <bool PER_TOKEN>
+__device__ __forceinline__ float encode_row_e4m3(const uint16_t* row, int lane, float tensor_scale,
+                                                 u32x2 (&codes)[2]) {
+  const u32x4* src = reinterpret_cast<const u32x4*>(row);
+  const int nchunk = lane < 8 ? 2 : 1;
+  float x[2][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    if (c < nchunk) {
+      const u32x4 w = src[lane + 64 * c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[c][2 * e] = float_of(w[e] << 16);
+        x[c][2 * e + 1] = float_of(w[e] & 0xffff0000u);
+        amax = fmaxf(amax, fmaxf(fabsf(x[c][2 * e]), fabsf(x[c][2 * e + 1])));
+      }
+    }
+  }
+  float scale = tensor_scale;
+  if (PER_TOKEN) {
+    amax = wave_max(amax);
+    scale = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    uint32_t lo = 0, hi = 0;
+    if (c < nchunk) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo |= float_to_e4m3(__fdiv_rn(x[c][e], scale)) << (8 * e);
+        hi |= float_to_e4m3(__fdiv_rn(x[c][4 + e], scale)) << (8 * e);
+      }
+    }
+    codes[c] = u32x2{lo, hi};
+  }
+  return scale;
+}
+
 // Reduction across the four 16-lane groups (lanes l, l^16, l^32, l^48), on
 // the VALU: permlane16_swap pairs rows 0/1 and 2/3, permlane32_swap pairs the
 // two halves of the wave.

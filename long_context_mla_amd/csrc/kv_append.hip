@@ -20,44 +20,12 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendArgs a) {
   page = min(max(page, 0), a.num_pages - 1);
   const int slot = pos % kPage;
 
-  // 72 chunks of 8 elements; lanes 0..7 take a second chunk
-  const u32x4* src = reinterpret_cast<const u32x4*>(a.kv_new + (int64_t)row * kD);
-  const int nchunk = lane < 8 ? 2 : 1;
-  float x[2][8];
-  float amax = 0.0f;
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    if (c < nchunk) {
-      const u32x4 w = src[lane + 64 * c];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[c][2 * e] = float_of(w[e] << 16);
-        x[c][2 * e + 1] = float_of(w[e] & 0xffff0000u);
-        amax = fmaxf(amax, fmaxf(fabsf(x[c][2 * e]), fabsf(x[c][2 * e + 1])));
-      }
-    }
-  }
-  float scale;
-  if (SCALE == kScaleToken) {
-    amax = wave_max(amax);
-    scale = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
-  } else {
-    scale = a.kv_scale[0];
-  }
+  u32x2 codes[2];
+  const float scale = encode_row_e4m3<SCALE == kScaleToken>(a.kv_new + (int64_t)row * kD, lane,
+                                                            SCALE == kScaleToken ? 1.0f : a.kv_scale[0], codes);
   uint8_t* dst = a.cache + ((int64_t)page * kPage + slot) * kD;
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    if (c < nchunk) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo |= float_to_e4m3(__fdiv_rn(x[c][e], scale)) << (8 * e);
-        hi |= float_to_e4m3(__fdiv_rn(x[c][4 + e], scale)) << (8 * e);
-      }
-      u32x2 v = {lo, hi};
-      *reinterpret_cast<u32x2*>(dst + 8 * (lane + 64 * c)) = v;
-    }
-  }
+  *reinterpret_cast<u32x2*>(dst + 8 * lane) = codes[0];
+  if (lane < 8) *reinterpret_cast<u32x2*>(dst + 8 * (lane + 64)) = codes[1];
   if (SCALE == kScaleToken && lane == 0) a.kv_scale[(int64_t)page * kPage + slot] = scale;
 }
 

@@ -28,6 +28,13 @@ struct DecodeArgs {
   float* lse;               // fp32 [B, R]
   int B, n_q, H, R, max_blocks, num_pages, pps, max_splits, n_rg;
   float sm_log2;            // softmax_scale * log2(e)
+  // Rows appended in the same launch (FP8 cache only; n_new = 0: none): bf16
+  // [B, n_new, 576] at positions seq_lens[b] - n_new .. seq_lens[b] - 1, and
+  // the writable cache / per-token scales they go to.
+  const uint16_t* kv_new;
+  int n_new;
+  uint8_t* cache_out;
+  float* scale_out;
 };
 
 struct CombineArgs {

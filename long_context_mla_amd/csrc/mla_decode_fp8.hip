@@ -227,6 +227,41 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     constexpr int KB = kD / 32;
     u32x4 kraw[KB / 2];  // this wave's K bytes of the next page, read ahead
 
+    // Rows appended in this launch that fall among this wave's 16 tokens of
+    // page it: the wave encodes each one exactly as kv_append_fp8 does and
+    // puts it over the row the copy brought (the cache still held the old
+    // contents); row group 0 also writes it, and its per-token scale, to the
+    // cache for later steps.  Both row groups compute the same bytes, so it
+    // does not matter which copy the other group's page read saw.
+    auto patch_new_rows = [&](int it, uint8_t* kv) {
+      const int t_first = (p_begin + it) * kPage + qw * 16;
+      const int first_new = L - a.n_new;
+      const int lo = max(first_new, t_first), hi = min(L, t_first + 16);
+      for (int pos = lo; pos < hi; ++pos) {
+        u32x2 codes[2];
+        const float sc = encode_row_e4m3<SCALE == kScaleToken>(
+            a.kv_new + ((int64_t)b * a.n_new + (pos - first_new)) * kD, lane, tscale, codes);
+        const int t = pos & (kPage - 1);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int c8 = lane + 64 * c;  // 8-byte chunk of the row
+          if (c == 0 || lane < 8)
+            *reinterpret_cast<u32x2*>(kv + (t * Z::NCH + Z::slot(t, c8 >> 1)) * 16 + 8 * (c8 & 1)) = codes[c];
+        }
+        if (SCALE == kScaleToken && lane == 0) s_scale[it % T::NBUF][t] = sc;
+        if (rg == 0) {
+          const int pg = min(max(load_const(a.block_table, bt_row + pos / kPage), 0), a.num_pages - 1);
+          uint8_t* dst = a.cache_out + ((int64_t)pg * kPage + t) * kD;
+          *reinterpret_cast<u32x2*>(dst + 8 * lane) = codes[0];
+          if (lane < 8) *reinterpret_cast<u32x2*>(dst + 8 * (lane + 64)) = codes[1];
+          if (SCALE == kScaleToken && lane == 0) a.scale_out[(int64_t)pg * kPage + t] = sc;
+        }
+      }
+      // the row loads and stores are counted like the copies: let them all
+      // finish so the later waits keep their meaning
+      if (lo < hi) wait_vmcnt<0>();
+    };
+
     // Wait for this wave's own share of page it, zero its rows past the end of
     // the request (they may hold anything, even NaN codes, and P V multiplies
     // them by zero weights), and read its K bytes.  Loads complete in order, so
@@ -245,6 +280,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
         for (int e = lane; e < (qw * 16 + 16 - t0) * (T::ROW_BYTES / 16); e += 64)
           junk[e] = u32x4{0u, 0u, 0u, 0u};
       }
+      if (a.n_new > 0) patch_new_rows(it, kv);
 #pragma unroll
       for (int i = 0; i < KB / 2; ++i) kraw[i] = *reinterpret_cast<const u32x4*>(kv + klane + 64 * i);
     };

@@ -1,6 +1,8 @@
 """One decode step over a paged latent cache: append the step's new rows (FP8
-cache), split-KV attention, then the split merge — three C-ABI calls on the
-current stream with buffers allocated once per batch shape."""
+cache), split-KV attention, then the split merge, on the current stream with
+buffers allocated once per batch shape.  On an FP8 cache the append rides in
+the decode launch (mla_decode_paged_append); fuse_append=False issues
+kv_append_fp8 and mla_decode_paged separately."""
 
 from __future__ import annotations
 
@@ -11,7 +13,8 @@ from . import _lib
 
 class DecodeStep:
     def __init__(self, B, n_q, H, max_blocks, max_seq_len, total_seq_len, device, num_cus=0,
-                 pages_per_split=None, max_splits=None):
+                 pages_per_split=None, max_splits=None, fuse_append=True):
+        self.fuse_append = fuse_append
         if pages_per_split is None or max_splits is None:
             pages_per_split, max_splits = _lib.mla_decode_plan(B, n_q, H, max_seq_len, total_seq_len,
                                                                num_cus)
@@ -41,6 +44,13 @@ class DecodeStep:
     def __call__(self, q, kv_cache, kv_scale, scale_mode, block_table, seq_lens, softmax_scale,
                  new_rows=None, stream=None):
         if new_rows is not None and new_rows.shape[1] > 0:
+            if self.fuse_append:
+                _lib.mla_decode_paged_append(new_rows, q, kv_cache, kv_scale, scale_mode, block_table,
+                                             seq_lens, softmax_scale, self.pps, self.max_splits,
+                                             self.o_partial, self.lse_partial, self.out, self.lse,
+                                             stream=stream)
+                self.combine(seq_lens, stream)
+                return self.out, self.lse
             _lib.kv_append_fp8(new_rows, kv_cache, kv_scale, scale_mode, block_table, seq_lens,
                                stream=stream)
         self.decode(q, kv_cache, kv_scale, scale_mode, block_table, seq_lens, softmax_scale, stream)

@@ -113,6 +113,38 @@ def test_append_matches_oracle_bit_exact():
             assert np.array_equal(scale.cpu().numpy(), ref_s)
 
 
+@pytest.mark.parametrize("mode", ["token", "tensor"])
+def test_fused_append_equals_separate(mode):
+    """mla_decode_paged_append leaves the cache exactly as kv_append_fp8 does and
+    decodes bit-identically to kv_append_fp8 + mla_decode_paged: new rows that
+    straddle a page boundary (so land in two splits when each page is a split),
+    fill a page's end, or sit in a request's first page."""
+    import long_context_mla_amd as mla
+
+    w = synth.custom(f"fused_{mode}", B=3, n_q=4, H=64, context_lens=(62, 700, 1), cache_dtype="fp8",
+                     scale_mode=mode, seed=31)
+    log(f"fused append {mode}: L={w.seq_lens.tolist()}")
+    ref_o, ref_l = oracle_decode(w)
+    max_pages = int(-(-w.seq_lens.max() // 64))
+    for pps, ms in [(None, None), (1, max_pages), (max_pages, 1), (3, -(-max_pages // 3))]:
+        outs = []
+        for fuse in (False, True):
+            g = GpuState(w)
+            st = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(),
+                                g.device, pages_per_split=pps, max_splits=ms, fuse_append=fuse)
+            o, l = st(g.q, g.cache, g.kv_scale, g.scale_mode, g.block_table, g.seq_lens, w.softmax_scale,
+                      new_rows=g.new_rows)
+            torch.cuda.synchronize()
+            outs.append((bf16_tensor_to_f64(o), l.cpu().double().numpy(), g.cache.cpu().numpy(),
+                         g.kv_scale.cpu().numpy()))
+        (oa, la, ca, sa), (ob, lb, cb, sb) = outs
+        tag = f"{mode} pps={pps} splits={ms}"
+        assert np.array_equal(ca, cb), f"{tag}: cache differs at {np.argwhere(ca != cb)[:5]}"
+        assert np.array_equal(sa, sb), f"{tag}: scales differ"
+        assert np.array_equal(oa, ob) and np.array_equal(la, lb), f"{tag}: outputs differ"
+        compare(ob, lb, ref_o, ref_l, tag=f"fused {tag}")
+
+
 def test_one_visible_token_returns_its_value():
     """L = 1: the only weight is 1, so out is the (dequantised) row itself."""
     for dtype, mode in (("fp8", "tensor"), ("fp8", "token"), ("bf16", "none")):
