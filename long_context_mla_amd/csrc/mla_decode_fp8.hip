@@ -183,8 +183,11 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
       const int pg = min(max(__builtin_amdgcn_readlane(ids, it & 63), 0), a.num_pages - 1);
       dma_src = a.cache + (int64_t)pg * T::PAGE_BYTES;
       dma_dst = lds_addr(&s_kv[it % T::NBUF][0]) + qw * T::LOADS * 1024;
-      if (SCALE == kScaleToken)
-        lds_dma4(a.kv_scale + (int64_t)pg * kPage, lane * 4, lds_addr(&s_scale[it % T::NBUF][0]));
+      // the scales of the wave's own 16 tokens only: a row appended in this
+      // launch overwrites its scale in LDS after the wave's wait, and another
+      // wave's copy of the same word could still land after that
+      if (SCALE == kScaleToken && lane < 16)
+        lds_dma4(a.kv_scale + (int64_t)pg * kPage + qw * 16, lane * 4, lds_addr(&s_scale[it % T::NBUF][qw * 16]));
     };
     auto dma_load = [&](int j) { lds_dma16(dma_src, goff[j], dma_dst + j * 1024); };
     auto prologue = [&]() {
@@ -334,7 +337,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
         const float mr = m0[rb] == -INFINITY ? 0.0f : m0[rb];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          y[rb][i] = __builtin_fmaf(S[rb][i], SCALE == kScaleToken ? cs[i] : coef, -mr);
+          y[rb][i] = scaled_minus(S[rb][i], SCALE == kScaleToken ? cs[i] : coef, mr);
       }
       if (tbase + kPage > lim_lo) {
 #pragma unroll
