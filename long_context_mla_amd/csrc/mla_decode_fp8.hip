@@ -37,7 +37,20 @@ namespace mla {
 template <int SCALE>
 __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   using T = Tile<kFp8>;
-  using Z = Swz<kFp8>;
+  // LDS layout of a staged page (36 16-byte chunks per token): token t's
+  // chunk c sits in 16-byte slot pslot(t, c).  Each 16-token quarter (the
+  // tokens one score wave copies and reads) takes 576 consecutive slots, in
+  // nine groups of 64: group c / 4 holds chunks 4(c / 4) .. +3 of the 16
+  // tokens, four per token, the chunk's two low bits XORed with
+  // F(t % 16) = {0, 2, 3, 1}[(t % 16) / 4].  One page copy instruction then
+  // fills one group (lane l: token l / 4, chunk (l % 4) ^ F), and both the
+  // QK^T operand reads (16 B: token, chunk) and the transposing P V reads
+  // (8 B: 8 tokens of one chunk) hit distinct LDS banks.
+  auto pswz = [](int tl) { return (0x78 >> (2 * ((tl >> 2) & 3))) & 3; };
+  auto pslot = [&](int t, int c) {
+    const int tl = t & 15;
+    return (t >> 4) * 576 + (c >> 2) * 64 + tl * 4 + ((c & 3) ^ pswz(tl));
+  };
   static_assert(T::NBUF == 4 && T::DIST == 2, "four page buffers, two pages in flight");
   __shared__ __attribute__((aligned(16))) uint8_t s_kv[T::NBUF][T::PAGE_BYTES];
   __shared__ __attribute__((aligned(16))) float s_scale[T::NBUF][kPage];
@@ -162,15 +175,12 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     const int lim_lo = L - a.n_q + r0 / a.H + 1;
 
     constexpr int LPP = T::LOADS + (SCALE == kScaleToken ? 1 : 0);  // loads per page per wave
-    // each lane's source offsets inside a page for its LOADS LDS chunk slots;
-    // wave w copies tokens 16w .. 16w+15, the rows its own QK^T reads
-    uint32_t goff[T::LOADS];
-#pragma unroll
-    for (int j = 0; j < T::LOADS; ++j) {
-      const int slot = (qw * T::LOADS + j) * 64 + lane;
-      const int t = slot / Z::NCH;
-      goff[j] = t * T::ROW_BYTES + Z::chunk_of_slot(t, slot - t * Z::NCH) * 16;
-    }
+    // wave w copies tokens 16w .. 16w+15 (the rows its own QK^T reads): copy
+    // instruction j fills slot group j of its quarter, lane l taking token
+    // 16w + l/4's chunk 4j + ((l % 4) ^ F), at source byte goff + 64 j
+    static_assert(T::LOADS == 9 && T::ROW_BYTES == 576, "nine copies of 16 tokens x 4 chunks");
+    const uint32_t goff =
+        (uint32_t)((qw * 16 + (lane >> 2)) * T::ROW_BYTES + ((lane & 3) ^ pswz(lane >> 2)) * 16);
     // Page p_begin + it (and its scales) HBM -> its LDS buffer, two pages
     // ahead of its use.  dma_page picks the page and copies the scales;
     // dma_load(j) issues this wave's j-th 16-byte load of it.  Inside the loop
@@ -189,7 +199,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
       if (SCALE == kScaleToken && lane < 16)
         lds_dma4(a.kv_scale + (int64_t)pg * kPage + qw * 16, lane * 4, lds_addr(&s_scale[it % T::NBUF][qw * 16]));
     };
-    auto dma_load = [&](int j) { lds_dma16(dma_src, goff[j], dma_dst + j * 1024); };
+    auto dma_load = [&](int j) { lds_dma16(dma_src + 64 * j, goff, dma_dst + j * 1024); };
     auto prologue = [&]() {
 #pragma unroll
       for (int k = 0; k < T::DIST; ++k)
@@ -226,7 +236,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     float lsum[2] = {0.0f, 0.0f};           // this lane's share of the softmax sums (fp32 P)
     float lnrm[2] = {0.0f, 0.0f};           // the same over the bf16-rounded P that PV uses
     const int tok = qw * 16 + m;            // this lane's token in QK^T
-    const uint32_t klane = (uint32_t)((tok * Z::NCH + Z::slot(tok, g)) * 16);
+    const uint32_t klane = (uint32_t)(pslot(tok, g) * 16);  // chunk 4i + g at + 1024 i
     constexpr int KB = kD / 32;
     u32x4 kraw[KB / 2];  // this wave's K bytes of the next page, read ahead
 
@@ -249,7 +259,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
         for (int c = 0; c < 2; ++c) {
           const int c8 = lane + 64 * c;  // 8-byte chunk of the row
           if (c == 0 || lane < 8)
-            *reinterpret_cast<u32x2*>(kv + (t * Z::NCH + Z::slot(t, c8 >> 1)) * 16 + 8 * (c8 & 1)) = codes[c];
+            *reinterpret_cast<u32x2*>(kv + pslot(t, c8 >> 1) * 16 + 8 * (c8 & 1)) = codes[c];
         }
         if (SCALE == kScaleToken && lane == 0) s_scale[it % T::NBUF][t] = sc;
         if (rg == 0) {
@@ -278,14 +288,18 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
       uint8_t* kv = s_kv[it % T::NBUF];
       const int nvalid = L - (p_begin + it) * kPage;
       if (nvalid < qw * 16 + 16) {
-        const int t0 = max(nvalid, qw * 16);
-        u32x4* junk = reinterpret_cast<u32x4*>(kv + t0 * T::ROW_BYTES);
-        for (int e = lane; e < (qw * 16 + 16 - t0) * (T::ROW_BYTES / 16); e += 64)
-          junk[e] = u32x4{0u, 0u, 0u, 0u};
+        // tokens tl0 .. 15 of this wave's quarter: slots tl0 * 4 .. 63 of each group
+        const int tl0 = max(nvalid - qw * 16, 0);
+        const int per = (16 - tl0) * 4;
+        u32x4* q = reinterpret_cast<u32x4*>(kv) + qw * 576 + tl0 * 4;
+        for (int e = lane; e < 9 * per; e += 64) {
+          const int grp = e / per;
+          q[grp * 64 + (e - grp * per)] = u32x4{0u, 0u, 0u, 0u};
+        }
       }
       if (a.n_new > 0) patch_new_rows(it, kv);
 #pragma unroll
-      for (int i = 0; i < KB / 2; ++i) kraw[i] = *reinterpret_cast<const u32x4*>(kv + klane + 64 * i);
+      for (int i = 0; i < KB / 2; ++i) kraw[i] = *reinterpret_cast<const u32x4*>(kv + klane + 1024 * i);
     };
     // S^T[token][row] = K Q^T for this wave's 16 tokens, all 32 rows: one MFMA
     // pair per k-block with the conversions of the next k-block between them.
@@ -486,15 +500,13 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
       for (int j = 0; j < 8; ++j) O[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     mfma_zero_o(O);
     // per-lane LDS offsets of the V reads: lane 2j+h of a 16-lane group
-    // addresses token 8g+j (+32 kt) of its wave's dims; the chunk slot of dims
-    // 128w + 64(db/4) + 16(db%4) is 8w + 4(db/4) + ((db%4) ^ f), f = (token/4)%4
+    // addresses token 8g+j (+32 kt) of its wave's dims; dims 128w + 64(db/4) +
+    // 16(db%4) are chunk 8w + 4(db/4) + db%4, at pslot + 1024 (db/4) + 18432 kt
     uint32_t voff[4];
     {
       const int t = g * 8 + (m >> 1);
-      const int f = (t >> 2) & 3;
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb)
-        voff[bb] = (uint32_t)((t * Z::NCH + qw * 8 + (bb ^ f)) * 16 + 8 * (m & 1));
+      for (int bb = 0; bb < 4; ++bb) voff[bb] = (uint32_t)(pslot(t, 8 * qw + bb) * 16 + 8 * (m & 1));
     }
     bf16x8 pv_p[2][2];  // [32-token half][row block]
     u32x2 pv_v[2][8];   // [32-token half][16-dim block]
@@ -509,7 +521,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
           pv_p[kt][rbp] = *reinterpret_cast<const bf16x8*>(pp + (rbp * 16 + m) * T::PSTRIDE + tok0 * 2);
 #pragma unroll
         for (int db = 0; db < 8; ++db)
-          pv_v[kt][db] = lds_read_tr8(kvp + voff[db & 3] + kt * 32 * T::ROW_BYTES + 64 * (db >> 2));
+          pv_v[kt][db] = lds_read_tr8(kvp + voff[db & 3] + kt * 32 * T::ROW_BYTES + 1024 * (db >> 2));
       }
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
