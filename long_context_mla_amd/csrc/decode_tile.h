@@ -28,26 +28,25 @@ struct Tile {
   static constexpr int KBATCH = 9;                 // BF16 K reads issued before their math
 };
 
-// LDS layout of a staged page: token t's 16-byte chunk c (of NCH per row) sits
-// in chunk slot t * NCH + slot(t, c).  FP8 rows (36 chunks) XOR the two low
-// chunk bits with (t / 4) % 4; BF16 rows (72 chunks) rotate by 3 * (t / 2).
-// Both make the 16-token operand reads of QK^T and the 8-token transposed
-// reads of PV hit distinct LDS banks.  The HBM -> LDS copy applies the inverse
-// mapping when it picks each lane's source chunk.
-template <int CACHE>
-struct Swz {
-  static constexpr int NCH = CACHE == kFp8 ? 36 : 72;
-  __device__ static __forceinline__ int rot(int t) {  // BF16 rotation, in [0, NCH)
+// LDS layout of a staged BF16 page: token t's 16-byte chunk c (of NCH = 72 per
+// row) sits in chunk slot t * NCH + slot(t, c), the row rotated by 3 * (t / 2)
+// chunks, so that the 16-token operand reads of QK^T and the 8-token
+// transposed reads of PV hit distinct LDS banks.  The HBM -> LDS copy applies
+// the inverse mapping when it picks each lane's source chunk.  (FP8 pages use
+// their own grouped layout, defined with their kernel.)
+struct SwzBf16 {
+  static constexpr int NCH = 72;
+  __device__ static __forceinline__ int rot(int t) {  // in [0, NCH)
     const int r = 3 * (t >> 1);
     return r >= NCH ? r - NCH : r;  // t < 64 keeps r < 2 * NCH
   }
   __device__ static __forceinline__ int slot(int t, int c) {
-    if constexpr (CACHE == kFp8) return c ^ ((t >> 2) & 3);
-    else { const int v = c + rot(t); return v >= NCH ? v - NCH : v; }
+    const int v = c + rot(t);
+    return v >= NCH ? v - NCH : v;
   }
   __device__ static __forceinline__ int chunk_of_slot(int t, int s) {
-    if constexpr (CACHE == kFp8) return s ^ ((t >> 2) & 3);
-    else { const int v = s - rot(t); return v < 0 ? v + NCH : v; }
+    const int v = s - rot(t);
+    return v < 0 ? v + NCH : v;
   }
 };
 

@@ -14,24 +14,27 @@
 // cache"); physical pages reached through per-request page maps (same page,
 // section "Protecting a shared KV cache").
 //
-// gfx950 design.  One 256-thread workgroup (4 waves, one per SIMD) per
-// (request, split, group of 32 query rows); one workgroup per CU.
-//  * Pages stream HBM -> LDS with LDS-DMA (global_load_lds, no VGPRs), NBUF
-//    deep.  Each lane picks its source chunk so that the page lands in a
-//    swizzled layout whose operand reads are free of bank conflicts.
+// This file holds the kernel for a BF16 cache and the dispatch; FP8 caches go
+// to the kernel in mla_decode_fp8.hip.
+//
+// BF16 kernel, gfx950 design.  One 256-thread workgroup (4 waves, one per
+// SIMD) per (request, split, group of 32 query rows); one workgroup per CU.
+//  * Pages stream HBM -> LDS with LDS-DMA (global_load_lds, no VGPRs), two
+//    buffers, one page in flight.  Each lane picks its source chunk so that
+//    the page lands in a rotated layout whose operand reads are free of bank
+//    conflicts.
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: wave w takes tokens 16w..16w+15
 //    of the page for all 32 rows; the rows' query stays in registers as bf16
-//    operands for the whole split.  FP8 codes become bf16 in registers
-//    (exact); scales are applied to the fp32 scores.
+//    operands for the whole split.
 //  * Softmax weights 2^(x - m0) use one reference per row, fixed from the
 //    split's first page (the only page that exchanges row maxima).  O is never
 //    rescaled: if a later score exceeds the reference by more than 2^64 the
 //    split restarts from its first page with the larger reference.
-//  * O += P V on MFMA with the accumulators in AGPRs: wave w takes output dims
-//    128w..128w+127; V is the first 512 columns of the same staged page, read
-//    with transposing LDS loads (ds_read_b64_tr_b8 / _b16).
+//  * O += P V on MFMA: wave w takes output dims 128w..128w+127; V is the first
+//    512 columns of the same staged page, read with transposing LDS loads
+//    (ds_read_b64_tr_b16).
 //  * Epilogue: O / l and the natural-log LSE, either final (one split) or as
-//    split partials for mla_decode_combine.
+//    bf16 split partials for mla_decode_combine.
 #include <type_traits>
 
 #include "decode_tile.h"
@@ -40,12 +43,10 @@
 
 namespace mla {
 
-template <int CACHE, int SCALE>
-__global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
-  using T = Tile<CACHE>;
-  using Z = Swz<CACHE>;
+__global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
+  using T = Tile<kBf16>;
+  using Z = SwzBf16;
   __shared__ __attribute__((aligned(16))) uint8_t s_kv[T::NBUF][T::PAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) float s_scale[T::NBUF][kPage];
   __shared__ __attribute__((aligned(16))) uint8_t s_p[2][kRows * T::PSTRIDE];
   __shared__ float s_red[4][kRows];   // per-wave row maxima (first page, restarts)
   __shared__ float s_lsum[4][kRows];
@@ -93,8 +94,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
   }
   const int p_end = split == a.max_splits - 1 ? n_pages : min(n_pages, p_begin + a.pps);
   const int n_it = p_end - p_begin;
-  const float tscale = SCALE == kScaleTensor ? load_const(a.kv_scale, 0) : 1.0f;
-  const float coef = a.sm_log2 * tscale;
+  const float coef = a.sm_log2;
 
   // ---- the query of the group's 32 rows, HBM -> LDS in one coalesced copy
   // shared by the four waves, into the page buffer that stays free until the
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
   }
   const int lim_lo = L - a.n_q + r0 / a.H + 1;
 
-  constexpr int LPP = T::LOADS + (SCALE == kScaleToken ? 1 : 0);  // loads per page per wave
+  constexpr int LPP = T::LOADS;  // loads per page per wave
   // each lane's source offsets inside a page for its LOADS LDS chunk slots;
   // wave w copies tokens 16w .. 16w+15, the rows its own QK^T reads
   uint32_t goff[T::LOADS];
@@ -155,8 +155,6 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
     const int pg = __builtin_amdgcn_readlane(ids, it & 63);
     dma_src = a.cache + (int64_t)pg * T::PAGE_BYTES;
     dma_dst = lds_addr(&s_kv[it % T::NBUF][0]) + wave * T::LOADS * 1024;
-    if (SCALE == kScaleToken)
-      lds_dma4(a.kv_scale + (int64_t)pg * kPage, lane * 4, lds_addr(&s_scale[it % T::NBUF][0]));
   };
   auto dma_part = [&](int part) {
 #pragma unroll
@@ -212,19 +210,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
   bool have_ref = false;
   int restarts = 0;
 
-  // per-lane LDS offsets of the PV operand reads (FP8): lane 2j+h of a 16-lane
-  // group addresses token 8g+j (+32 kt) of its wave's dims; the chunk slot of
-  // dims 128w + 64(db/4) + 16(db%4) is 8w + 4(db/4) + ((db%4) ^ f), f = (token/4)%4
-  uint32_t voff[4];
-  {
-    const int t = g * 8 + (m >> 1);
-    const int f = (t >> 2) & 3;
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
-      voff[bb] = (uint32_t)((t * Z::NCH + wave * 8 + (bb ^ f)) * 16 + 8 * (m & 1));
-  }
   const int tok = wave * 16 + m;  // this lane's token in QK^T
-  const uint32_t klane = (uint32_t)((tok * Z::NCH + Z::slot(tok, g)) * 16);  // FP8 K chunk base
 
   // ---- P V over this wave's 128 dims for the page in buffer kvp, with its
   // weights in P buffer pp; mid() runs between the two 32-token halves
@@ -238,49 +224,21 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
       // slots are tokens tok0 .. tok0+7 in both
       const int tok0 = kt * 32 + g * 8;
       bf16x8 pop[2];
-      u32x2 vraw[8][CACHE == kFp8 ? 1 : 2];
+      u32x2 vraw[8][2];
 #pragma unroll
       for (int rbp = 0; rbp < 2; ++rbp)
         pop[rbp] = *reinterpret_cast<const bf16x8*>(pp + (rbp * 16 + m) * T::PSTRIDE + tok0 * 2);
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        if constexpr (CACHE == kFp8) {
-          vraw[db][0] = lds_read_tr8(kvp + voff[db & 3] + kt * 32 * T::ROW_BYTES + 64 * (db >> 2));
-        } else {
-          // lane 4j+q of the group addresses token tok0+j (+4), elements dcol+4q .. +4
-          const int dcol = dim0 + db * 16;
-          const int c = (dcol >> 3) + ((m & 3) >> 1);
-          const int t0 = tok0 + (m >> 2), t1 = t0 + 4;
-          vraw[db][0] = lds_read_tr16(kvp + (t0 * Z::NCH + Z::slot(t0, c)) * 16 + 8 * (m & 1));
-          vraw[db][CACHE == kFp8 ? 0 : 1] = lds_read_tr16(kvp + (t1 * Z::NCH + Z::slot(t1, c)) * 16 + 8 * (m & 1));
-        }
+        // lane 4j+q of the group addresses token tok0+j (+4), elements dcol+4q .. +4
+        const int dcol = dim0 + db * 16;
+        const int c = (dcol >> 3) + ((m & 3) >> 1);
+        const int t0 = tok0 + (m >> 2), t1 = t0 + 4;
+        vraw[db][0] = lds_read_tr16(kvp + (t0 * Z::NCH + Z::slot(t0, c)) * 16 + 8 * (m & 1));
+        vraw[db][1] = lds_read_tr16(kvp + (t1 * Z::NCH + Z::slot(t1, c)) * 16 + 8 * (m & 1));
       }
       __builtin_amdgcn_sched_barrier(0);  // reads ahead of the math
-      if constexpr (CACHE == kFp8) {
-        // per 16-dim block: its MFMA pair with the conversions of the next
-        // block between them (two operand register sets)
-        uint32_t d[2][4];
-        d[0][0] = cvt_e4m3_lo(vraw[0][0].x);
-        d[0][1] = cvt_e4m3_hi(vraw[0][0].x);
-        d[0][2] = cvt_e4m3_lo(vraw[0][0].y);
-        d[0][3] = cvt_e4m3_hi(vraw[0][0].y);
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          const bf16x8 vop = bf16x8_of(d[db & 1]);
-          uint32_t (&nx)[4] = d[(db + 1) & 1];
-          mfma_vvv_w(O[0][db], pop[0], vop);
-          if (db + 1 < 8) {
-            nx[0] = cvt_e4m3_lo(vraw[db + 1][0].x);
-            nx[1] = cvt_e4m3_hi(vraw[db + 1][0].x);
-          }
-          mfma_vvv(O[1][db], pop[1], vop);
-          if (db + 1 < 8) {
-            nx[2] = cvt_e4m3_lo(vraw[db + 1][0].y);
-            nx[3] = cvt_e4m3_hi(vraw[db + 1][0].y);
-          }
-        }
-        mfma_drain_o(O, pop[0], pop[1], bf16x8_of(d[1]));
-      } else {
+      {
         // convert two V blocks into distinct registers, then issue their four MFMAs
 #pragma unroll
         for (int d0 = 0; d0 < 8; d0 += 2) {
@@ -288,8 +246,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
           for (int d = 0; d < 2; ++d)
             vop[d] = __builtin_bit_cast(bf16x8, u32x4{vraw[d0 + d][0].x, vraw[d0 + d][0].y,
-                                                      vraw[d0 + d][CACHE == kFp8 ? 0 : 1].x,
-                                                      vraw[d0 + d][CACHE == kFp8 ? 0 : 1].y});
+                                                      vraw[d0 + d][1].x, vraw[d0 + d][1].y});
 #pragma unroll
           for (int d = 0; d < 2; ++d)
 #pragma unroll
@@ -301,82 +258,9 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
   };
   auto no_mid = [] {};
 
-  // FP8 P V split in two: pv_read issues every LDS read of a page's P V (both
-  // 32-token halves) so that their latency hides behind other work, pv_math
-  // consumes them.  Operand layouts as in pv above.
-  bf16x8 pv_p[2][2];   // [half][row block]
-  u32x2 pv_v[2][8];    // [half][16-dim block]
-  auto pv_read = [&](const uint8_t* kvp, const uint8_t* pp) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int tok0 = kt * 32 + g * 8;
-#pragma unroll
-      for (int rbp = 0; rbp < 2; ++rbp)
-        pv_p[kt][rbp] = *reinterpret_cast<const bf16x8*>(pp + (rbp * 16 + m) * T::PSTRIDE + tok0 * 2);
-#pragma unroll
-      for (int db = 0; db < 8; ++db)
-        pv_v[kt][db] = lds_read_tr8(kvp + voff[db & 3] + kt * 32 * T::ROW_BYTES + 64 * (db >> 2));
-    }
-  };
-  auto pv_math = [&](auto mid) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      if (kt == 1) mid();
-      uint32_t d[2][4];
-      d[0][0] = cvt_e4m3_lo(pv_v[kt][0].x);
-      d[0][1] = cvt_e4m3_hi(pv_v[kt][0].x);
-      d[0][2] = cvt_e4m3_lo(pv_v[kt][0].y);
-      d[0][3] = cvt_e4m3_hi(pv_v[kt][0].y);
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const bf16x8 vop = bf16x8_of(d[db & 1]);
-        uint32_t (&nx)[4] = d[(db + 1) & 1];
-        mfma_vvv_w(O[0][db], pv_p[kt][0], vop);
-        if (db + 1 < 8) {
-          nx[0] = cvt_e4m3_lo(pv_v[kt][db + 1].x);
-          nx[1] = cvt_e4m3_hi(pv_v[kt][db + 1].x);
-        }
-        mfma_vvv(O[1][db], pv_p[kt][1], vop);
-        if (db + 1 < 8) {
-          nx[2] = cvt_e4m3_lo(pv_v[kt][db + 1].y);
-          nx[3] = cvt_e4m3_hi(pv_v[kt][db + 1].y);
-        }
-      }
-      mfma_drain_o(O, pv_p[kt][0], pv_p[kt][1], bf16x8_of(d[1]));
-    }
-  };
-
   // ---- S^T[token][row] = K Q^T for this wave's 16 tokens of the page, all
-  // 32 rows: from the FP8 bytes already read (kraw) or, BF16, from LDS
+  // 32 rows, K straight from LDS
   constexpr int KB = kD / 32;
-  u32x4 kraw[KB / 2];
-  auto qk_fp8 = [&](f32x4 (&S)[2]) {
-    // One MFMA pair per k-block, the conversions of the next k-block
-    // between them (software pipelined over two operand register sets).
-    auto lo_word = [&](int kb) { const u32x4 w = kraw[kb >> 1]; return (kb & 1) ? w[2] : w[0]; };
-    auto hi_word = [&](int kb) { const u32x4 w = kraw[kb >> 1]; return (kb & 1) ? w[3] : w[1]; };
-    uint32_t d[2][4];
-    d[0][0] = cvt_e4m3_lo(lo_word(0));
-    d[0][1] = cvt_e4m3_hi(lo_word(0));
-    d[0][2] = cvt_e4m3_lo(hi_word(0));
-    d[0][3] = cvt_e4m3_hi(hi_word(0));
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const bf16x8 kop = bf16x8_of(d[kb & 1]);
-      uint32_t (&nx)[4] = d[(kb + 1) & 1];
-      if (kb == 0) mfma_vva0_w(S[0], kop, qop[0][0]); else mfma_vva_w(S[0], kop, qop[0][kb]);
-      if (kb + 1 < KB) {
-        nx[0] = cvt_e4m3_lo(lo_word(kb + 1));
-        nx[1] = cvt_e4m3_hi(lo_word(kb + 1));
-      }
-      if (kb == 0) mfma_vva0(S[1], kop, qop[1][0]); else mfma_vva(S[1], kop, qop[1][kb]);
-      if (kb + 1 < KB) {
-        nx[2] = cvt_e4m3_lo(hi_word(kb + 1));
-        nx[3] = cvt_e4m3_hi(hi_word(kb + 1));
-      }
-    }
-    mfma_drain_s(S[0], S[1], bf16x8_of(d[(KB - 1) & 1]));
-  };
   auto qk_bf16 = [&](const uint8_t* kv, f32x4 (&S)[2]) {
 #pragma unroll
     for (int k0 = 0; k0 < KB; k0 += T::KBATCH) {
@@ -403,22 +287,14 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
   // past each row's causal limit, and the running maxima.  Lane holds tokens
   // 16w + 4g + i of rows rb*16 + m.
   float y[2][4];
-  f32x4 sc = {1.0f, 1.0f, 1.0f, 1.0f};
   auto scores = [&](const f32x4 (&S)[2], int it) {
-    const int buf = it % T::NBUF;
     const int tbase = (p_begin + it) * kPage;
-    float cs[4];
-    if (SCALE == kScaleToken) {
-      sc = *reinterpret_cast<const f32x4*>(&s_scale[buf][wave * 16 + 4 * g]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cs[i] = coef * sc[i];
-    }
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const float mr = m0[rb] == -INFINITY ? 0.0f : m0[rb];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        y[rb][i] = scaled_minus(S[rb][i], SCALE == kScaleToken ? cs[i] : coef, mr);
+        y[rb][i] = scaled_minus(S[rb][i], coef, mr);
     }
     if (tbase + kPage > lim_lo) {
       // the page reaches a row's causal limit or the end of the request
@@ -460,15 +336,9 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(y[rb][i]);
       uint32_t pk[2];
-      if (SCALE == kScaleToken) {
-        // the per-token V scale rides on the weight; the sums stay unscaled
 #pragma unroll
-        for (int i = 0; i < 2; ++i) pk[i] = pack_bf16x2(e[2 * i] * sc[2 * i], e[2 * i + 1] * sc[2 * i + 1]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) pk[i] = pack_bf16x2(e[2 * i], e[2 * i + 1]);
-        lnrm[rb] = dot2_bf16_ones(pk[1], dot2_bf16_ones(pk[0], lnrm[rb]));
-      }
+      for (int i = 0; i < 2; ++i) pk[i] = pack_bf16x2(e[2 * i], e[2 * i + 1]);
+      lnrm[rb] = dot2_bf16_ones(pk[1], dot2_bf16_ones(pk[0], lnrm[rb]));
       lsum[rb] += (e[0] + e[1]) + (e[2] + e[3]);
       *reinterpret_cast<u32x2*>(s_p[it & 1] + (rb * 16 + m) * T::PSTRIDE + (wave * 16 + 4 * g) * 2) =
           u32x2{pk[0], pk[1]};
@@ -551,7 +421,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const float ls = group4_sum(lsum[rb]);
-    const float ln = SCALE == kScaleToken ? ls : group4_sum(lnrm[rb]);
+    const float ln = group4_sum(lnrm[rb]);
     const int row = rb * 16 + m;
     if (g == 0) {
       s_lsum[wave][row] = ls;
@@ -572,7 +442,7 @@ __global__ __launch_bounds__(256, 1) void decode_split_kernel(DecodeArgs a) {
       const float ln = s_lnrm[0][row] + s_lnrm[1][row] + s_lnrm[2][row] + s_lnrm[3][row];
       // the output is a weighted mean with the bf16 weights PV used; the LSE
       // uses the fp32 weights
-      const float inv = ln > 0.0f ? tscale / ln : 0.0f;
+      const float inv = ln > 0.0f ? 1.0f / ln : 0.0f;
       const float mr = s_m0[row] == -INFINITY ? 0.0f : s_m0[row];
       const float lse_nat = lt > 0.0f ? (mr + __log2f(lt)) * kLn2 : -INFINITY;
       if (a.max_splits == 1) {
@@ -596,28 +466,13 @@ int decode_rows_per_group(int B, int R) {
   return kRows;
 }
 
-template <int CACHE>
-static hipError_t launch_cache(const DecodeArgs& a, int scale_mode, hipStream_t stream) {
-  const dim3 grid(((a.max_splits + 7) / 8) * 8 * a.n_rg, a.B), block(256);
-  switch (scale_mode) {
-    case kScaleTensor:
-      hipLaunchKernelGGL((decode_split_kernel<CACHE, kScaleTensor>), grid, block, 0, stream, a);
-      break;
-    case kScaleToken:
-      hipLaunchKernelGGL((decode_split_kernel<CACHE, kScaleToken>), grid, block, 0, stream, a);
-      break;
-    default:
-      hipLaunchKernelGGL((decode_split_kernel<CACHE, kScaleNone>), grid, block, 0, stream, a);
-      break;
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_decode(const DecodeArgs& a0, int cache_kind, int scale_mode, hipStream_t stream) {
   DecodeArgs a = a0;
   a.n_rg = (a.R + kRows - 1) / kRows;
   if (cache_kind == kFp8) return launch_decode_fp8(a, scale_mode, stream);
-  return launch_cache<kBf16>(a, kScaleNone, stream);
+  const dim3 grid(((a.max_splits + 7) / 8) * 8 * a.n_rg, a.B), block(256);
+  hipLaunchKernelGGL(decode_bf16_kernel, grid, block, 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace mla

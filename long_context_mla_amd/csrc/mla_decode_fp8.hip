@@ -22,6 +22,10 @@
 // at the same time.  Two waves per SIMD leave 256 registers per wave; the
 // kernel uses VGPRs only (no AGPRs), so all 256 are available to either role.
 //
+// mla_decode_paged_append runs the same kernel with the step's new rows: the
+// score wave that owns a new row's slot encodes it into its LDS copy of the
+// page (as kv_append_fp8 would), and row group 0 writes it to the cache.
+//
 // Softmax: one fixed reference per row and split (the first page's maximum),
 // weights 2^(y - m0); a weight above 2^64 restarts the split with a larger
 // reference (all waves together).  The output divides by the sum of the bf16
