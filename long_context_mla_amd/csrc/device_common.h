@@ -130,6 +130,15 @@ __device__ __forceinline__ float encode_row_e4m3(const uint16_t* row, int lane, 
   return scale;
 }
 
+// max(a, b, c) in one instruction.  fmaxf chains get an extra canonicalising
+// max per operand that is not provably a quiet value (a masked score is a
+// select), which doubles the work of a running maximum.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // x * c - r rounded twice, never fused into one FMA (the compiler contracts
 // a product and a difference unless the product passes through an opaque
 // statement): the token holding a row's reference then gets an exponent of

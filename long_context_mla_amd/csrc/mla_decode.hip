@@ -306,7 +306,7 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
-      ymax[rb] = fmaxf(fmaxf(ymax[rb], fmaxf(y[rb][0], y[rb][1])), fmaxf(y[rb][2], y[rb][3]));
+      ymax[rb] = max3f(max3f(ymax[rb], y[rb][0], y[rb][1]), y[rb][2], y[rb][3]);
   };
   // first page of the split: the reference of each row is its page max
   auto first_ref = [&]() {

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   __shared__ float s_lsum[4][kRows];
   __shared__ float s_lnrm[4][kRows];
   __shared__ float s_m0[kRows];
-  __shared__ __attribute__((aligned(16))) int s_flag[2][4];
+  __shared__ __attribute__((aligned(16))) uint8_t s_flag[2][4];  // [page parity][score wave]
 
   // One round trip for the launch arguments the first loads need: without
   // this the compiler fetches them in dependent batches.
@@ -143,11 +143,17 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   const float tscale = SCALE == kScaleTensor ? load_const(a.kv_scale, 0) : 1.0f;
   bool have_ref = false;
   int restarts = 0;
-  auto flag_word = [&](int it) {
-    const int4 f = *reinterpret_cast<const int4*>(&s_flag[it & 1][0]);
-    return f.x | f.y | f.z | f.w;
+  // The four score waves' restart flags of page it, one byte each, read as one
+  // word.  They are read right after the barrier that publishes them and
+  // looked at only after the next block of MFMA work has been issued:
+  // settle() ties the word to that point, so the LDS latency of the read is
+  // not waited for at the barrier.
+  auto flag_words = [&](int it) { return *reinterpret_cast<const uint32_t*>(&s_flag[it & 1][0]); };
+  auto settle = [](uint32_t& f) {
+    asm volatile("" : "+v"(f));
+    f = __builtin_amdgcn_readfirstlane(f);  // uniform again for the branch on it
   };
-  auto flagged = [&](int it) { return flag_word(it) && restarts < kMaxRestarts; };
+  auto restart_asked = [&](uint32_t f) { return f != 0u && restarts < kMaxRestarts; };
 
   if (scorer) {
     // =====================================================================
@@ -366,7 +372,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
       }
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
-        ymax[rb] = fmaxf(fmaxf(ymax[rb], fmaxf(y[rb][0], y[rb][1])), fmaxf(y[rb][2], y[rb][3]));
+        ymax[rb] = max3f(max3f(ymax[rb], y[rb][0], y[rb][1]), y[rb][2], y[rb][3]);
     };
     // softmax, part 2: weights 2^y as bf16 P into LDS, the sums, and the flag
     // that asks for a restart when a weight would exceed 2^64
@@ -392,7 +398,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
       }
       const bool over = ymax[0] > kRefSlack || ymax[1] > kRefSlack;
       const bool any_over = __any(over);
-      if (lane == 0) s_flag[it & 1][qw] = any_over;
+      if (lane == 0) s_flag[it & 1][qw] = any_over ? 1 : 0;
     };
 
     for (;;) {
@@ -436,26 +442,28 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
       // LDS latency of the read stays off the page's critical path.  On a
       // restart that work (and a copy already issued) is simply dropped; the
       // output waves leave their loop after the same barrier.
-      int fw = flag_word(0);
+      uint32_t fw = flag_words(0);
       bool again = false;
       auto page = [&](int it, auto dma_c) {  // false: leave for a restart
         constexpr bool dma = decltype(dma_c)::value;
         if constexpr (dma) dma_page(it + T::DIST);
         f32x4 S[2];
         qk(S, dma_c);
-        if (fw && restarts < kMaxRestarts) return false;
+        settle(fw);
+        if (restart_asked(fw)) return false;
         if (it + 1 < n_it) k_read(it + 1, dma);
         scores(S, it);
         weights(it);
         __syncthreads();  // (4) P and flags of page it are in LDS; page it - 1 is consumed
-        fw = flag_word(it);
+        fw = flag_words(it);
         return true;
       };
       int it = 1;
       bool ok = true;
       for (; ok && it + T::DIST < n_it; ++it) ok = page(it, std::true_type{});
       for (; ok && it < n_it; ++it) ok = page(it, std::false_type{});
-      again = !ok || (fw && restarts < kMaxRestarts);
+      if (ok) settle(fw);
+      again = !ok || restart_asked(fw);
       if (!again) break;
       // A weight would exceed 2^64: restart the split with a reference raised
       // to each row's running maximum.
@@ -560,11 +568,24 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
         have_ref = true;
       }
       __syncthreads();  // (3)
-      bool again = flagged(0);
-      for (int it = 1; it < n_it && !again; ++it) {
+      // Page it - 1's flags are looked at after P V of page it - 1 has been
+      // issued; when they ask for a restart that P V is wasted work (its
+      // operands are valid) and O is cleared below.
+      uint32_t fo = flag_words(0);
+      bool again = false;
+      for (int it = 1; it < n_it; ++it) {
         pv(it - 1);
+        settle(fo);
+        if (restart_asked(fo)) {
+          again = true;
+          break;
+        }
         __syncthreads();  // (4)
-        again = flagged(it);
+        fo = flag_words(it);
+      }
+      if (!again) {
+        settle(fo);
+        again = restart_asked(fo);
       }
       if (!again) {
         pv(n_it - 1);
