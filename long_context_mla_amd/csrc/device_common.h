@@ -285,10 +285,14 @@ __device__ __forceinline__ void mfma_result_fence_v16(f32x4 (&o)[2][8]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : MLA_O16(o));
 }
 // Zeroes the sixteen P V accumulators in place with MFMAs on zero operands,
-// in one statement that also waits out their latency.
+// in one statement that also waits out their latency.  The compiler may
+// materialise the zero operand with VALU moves right before the statement,
+// so it starts with the wait states an MFMA needs after a VALU write of its
+// source registers.
 __device__ __forceinline__ void mfma_zero_o(f32x4 (&o)[2][8]) {
   const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   asm volatile(
+      "s_nop 2\n\t"
       "v_mfma_f32_16x16x32_bf16 %0, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %1, %16, %16, 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %2, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %3, %16, %16, 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %4, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %5, %16, %16, 0\n\t"

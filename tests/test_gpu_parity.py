@@ -300,3 +300,29 @@ def test_long_split_repeatable(scale_mode):
         for o, l in runs[1:]:
             assert np.array_equal(o, runs[0][0]) and np.array_equal(l, runs[0][1]), f"pps={pps}"
         compare(runs[0][0], runs[0][1], ref_o, ref_l, tag=f"long split pps={pps} splits={ms}")
+
+
+@pytest.mark.parametrize("cache_dtype", ["fp8", "bf16"])
+def test_restart_on_late_large_scores(cache_dtype):
+    """A key planted along its head's query (logit about 60 log2-units per unit of
+    gain) in a page after the split's first one pushes a weight past 2^64 of the
+    first-page reference: the split restarts with a raised reference.  Two heads
+    with needles in different late pages restart a split twice; on FP8 one
+    needle sits in the row appended by the same launch."""
+    needles = [(0, 700, 3, 1.5), (0, 2100, 17, 1.5), (1, 1234, 40, 1.4)]
+    kw = dict(scale_mode="token", append=1) if cache_dtype == "fp8" else {}
+    lens = (3000, 1900)
+    if cache_dtype == "fp8":
+        needles.append((1, 1900, 9, 1.5))  # the appended row (positions are counted from 0)
+    w = synth.custom(f"restart_{cache_dtype}", B=2, n_q=1, H=64, context_lens=lens,
+                     cache_dtype=cache_dtype, seed=12, needles=tuple(needles), **kw)
+    log(f"restart {cache_dtype}: L={w.seq_lens.tolist()}")
+    g = GpuState(w)
+    ref_o, ref_l = oracle_decode(w)
+    out, lse = g.step()
+    summ = compare(out, lse, ref_o, ref_l, tag=f"restart {cache_dtype} planned")
+    assert summ["max_ref"] > 1.0  # the needles dominate their heads
+    npg = int(-(-w.seq_lens.max() // 64))
+    for pps, ms in [(npg, 1), (20, -(-npg // 20)), (1, npg)]:
+        o, l = g.decode_only(pps, ms)
+        compare(o, l, ref_o, ref_l, tag=f"restart {cache_dtype} pps={pps} splits={ms}")
