@@ -139,16 +139,6 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return r;
 }
 
-// x * c - r rounded twice, never fused into one FMA (the compiler contracts
-// a product and a difference unless the product passes through an opaque
-// statement): the token holding a row's reference then gets an exponent of
-// exactly 0, and every kernel forms exponents the same way.
-__device__ __forceinline__ float scaled_minus(float x, float c, float r) {
-  float t = x * c;
-  asm("" : "+v"(t));
-  return t - r;
-}
-
 // Reduction across the four 16-lane groups (lanes l, l^16, l^32, l^48), on
 // the VALU: permlane16_swap pairs rows 0/1 and 2/3, permlane32_swap pairs the
 // two halves of the wave.

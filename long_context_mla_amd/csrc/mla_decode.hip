@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
       const float mr = m0[rb] == -INFINITY ? 0.0f : m0[rb];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        y[rb][i] = scaled_minus(S[rb][i], coef, mr);
+        y[rb][i] = __builtin_fmaf(S[rb][i], coef, -mr);
     }
     if (tbase + kPage > lim_lo) {
       // the page reaches a row's causal limit or the end of the request

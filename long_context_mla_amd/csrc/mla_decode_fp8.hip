@@ -361,7 +361,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
         const float mr = m0[rb] == -INFINITY ? 0.0f : m0[rb];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          y[rb][i] = scaled_minus(S[rb][i], SCALE == kScaleToken ? cs[i] : coef, mr);
+          y[rb][i] = __builtin_fmaf(S[rb][i], SCALE == kScaleToken ? cs[i] : coef, -mr);
       }
       if (tbase + kPage > lim_lo) {
 #pragma unroll
