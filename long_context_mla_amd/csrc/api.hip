@@ -38,7 +38,7 @@ int decode_impl(const void* q, const void* kv_cache, int cache_dtype, const floa
   const int R = n_q * H;
   const int rows = mla::decode_rows_per_group(B, R);
   const int n_rg = (R + rows - 1) / rows;
-  if (((int64_t)max_splits + 7) / 8 * 8 * n_rg > kMaxGrid) return MLA_ERR_BAD_SHAPE;
+  if (mla::decode_grid_size(B, max_splits, n_rg) > kMaxGrid) return MLA_ERR_BAD_SHAPE;
   if (B == 0) return MLA_OK;
   if (!q || !kv_cache || !block_table || !seq_lens) return MLA_ERR_NULL_PTR;
   if (scale_mode != MLA_SCALE_NONE && !kv_scale) return MLA_ERR_NULL_PTR;
@@ -179,7 +179,7 @@ int mla_decode_plan(int B, int n_q, int H, int max_seq_len, int64_t total_seq_le
   if (pps < 1) pps = 1;
   if (pps > max_pages) pps = max_pages;
   int64_t splits = (max_pages + pps - 1) / pps;
-  if ((splits + 7) / 8 * 8 * n_rg > kMaxGrid) return MLA_ERR_BAD_SHAPE;
+  if (mla::decode_grid_size(B, splits, n_rg) > kMaxGrid) return MLA_ERR_BAD_SHAPE;
   *pages_per_split = (int)pps;
   *max_splits = (int)splits;
   return MLA_OK;

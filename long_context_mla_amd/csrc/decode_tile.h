@@ -50,6 +50,28 @@ struct SwzBf16 {
   }
 };
 
+// Workgroup -> (request, split, row group).  The hardware hands workgroup i
+// to XCD i % 8.  Work units u = b * max_splits + split go to the XCDs round
+// robin, so every XCD gets an equal share of the units whatever the split
+// count; the n_rg row groups of a unit (which read the same pages) are
+// consecutive workgroups of one XCD and share its L2.  Grid size:
+// decode_grid_size(B, max_splits, n_rg).
+struct WorkUnit {
+  int b, split, rg;
+  bool valid;
+};
+__device__ __forceinline__ WorkUnit decode_work_unit(int B, int max_splits, int n_rg) {
+  const int id = blockIdx.x;
+  const int j = id >> 3;
+  const int u = (j / n_rg) * 8 + (id & 7);
+  WorkUnit w;
+  w.rg = j % n_rg;
+  w.valid = u < B * max_splits;
+  w.b = w.valid ? u / max_splits : 0;
+  w.split = w.valid ? u - w.b * max_splits : 0;
+  return w;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");

@@ -49,6 +49,12 @@ struct CombineArgs {
 // Rows of the query matrix one decode workgroup owns (32 or 64).
 int decode_rows_per_group(int B, int R);
 
+// Workgroups of a decode launch (a 1-D grid): the B * max_splits work units
+// (request, split) padded to a multiple of the 8 XCDs, n_rg row groups each.
+inline int64_t decode_grid_size(int64_t B, int64_t max_splits, int64_t n_rg) {
+  return (B * max_splits + 7) / 8 * 8 * n_rg;
+}
+
 hipError_t launch_kv_append(const AppendArgs& a, int scale_mode, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int cache_kind, int scale_mode, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeArgs& a, int scale_mode, hipStream_t stream);

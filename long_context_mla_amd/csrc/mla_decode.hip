@@ -57,15 +57,9 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, g = lane >> 4;
-  // Workgroup -> (split, row group): workgroups are handed to the 8 XCDs round
-  // robin, so the row groups of one split (which read the same pages) are
-  // placed on the same XCD back to back and share its L2.
-  const int b = blockIdx.y;
-  const int xcd = blockIdx.x & 7;
-  const int kx = blockIdx.x >> 3;
-  const int rg = kx % a.n_rg;
-  const int split = (kx / a.n_rg) * 8 + xcd;
-  if (split >= a.max_splits) return;
+  const WorkUnit wu = decode_work_unit(a.B, a.max_splits, a.n_rg);
+  if (!wu.valid) return;
+  const int b = wu.b, split = wu.split, rg = wu.rg;
   const int L = min(max(load_const(a.seq_lens, b), 0), a.max_blocks * kPage);
   const int n_pages = (L + kPage - 1) / kPage;
   const int r0 = rg * kRows;
@@ -470,7 +464,7 @@ hipError_t launch_decode(const DecodeArgs& a0, int cache_kind, int scale_mode, h
   DecodeArgs a = a0;
   a.n_rg = (a.R + kRows - 1) / kRows;
   if (cache_kind == kFp8) return launch_decode_fp8(a, scale_mode, stream);
-  const dim3 grid(((a.max_splits + 7) / 8) * 8 * a.n_rg, a.B), block(256);
+  const dim3 grid((unsigned)decode_grid_size(a.B, a.max_splits, a.n_rg)), block(256);
   hipLaunchKernelGGL(decode_bf16_kernel, grid, block, 0, stream, a);
   return hipGetLastError();
 }

@@ -73,14 +73,9 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   const bool scorer = wave < 4;
   const int qw = wave & 3;  // index within the role
   const int m = lane & 15, g = lane >> 4;
-  // Workgroup -> (split, row group): the row groups of one split (which read
-  // the same pages) go to the same XCD back to back and share its L2.
-  const int b = blockIdx.y;
-  const int xcd = blockIdx.x & 7;
-  const int kx = blockIdx.x >> 3;
-  const int rg = kx % a.n_rg;
-  const int split = (kx / a.n_rg) * 8 + xcd;
-  if (split >= a.max_splits) return;
+  const WorkUnit wu = decode_work_unit(a.B, a.max_splits, a.n_rg);
+  if (!wu.valid) return;
+  const int b = wu.b, split = wu.split, rg = wu.rg;
   const int r0 = rg * kRows;
   const int p_begin = split * a.pps;
   const int64_t bt_row = (int64_t)b * a.max_blocks;
@@ -641,7 +636,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
 }
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, int scale_mode, hipStream_t stream) {
-  const dim3 grid(((a.max_splits + 7) / 8) * 8 * a.n_rg, a.B), block(512);
+  const dim3 grid((unsigned)decode_grid_size(a.B, a.max_splits, a.n_rg)), block(512);
   switch (scale_mode) {
     case kScaleTensor:
       hipLaunchKernelGGL((decode_fp8_kernel<kScaleTensor>), grid, block, 0, stream, a);
