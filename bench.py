@@ -199,7 +199,7 @@ def main():
     pps = args.pages_per_split or None
     ms = args.max_splits or None
     step = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(), dev,
-                          pages_per_split=pps, max_splits=ms)
+                          pages_per_split=pps, max_splits=ms, seq_lens_host=w.seq_lens)
     stream = torch.cuda.current_stream()
 
     def run(i, ev=None, st=None):

@@ -182,6 +182,21 @@ int mla_decode_combine(const void* o_partial, const float* lse_partial, const in
 int mla_decode_plan(int B, int n_q, int H, int max_seq_len, int64_t total_seq_len, int num_cus,
                     int* pages_per_split, int* max_splits);
 
+/*
+ * mla_decode_plan_lens — host-only split plan from the batch's lengths.
+ *   seq_lens   host int32 [B], the L_b of the coming launch (after its append).
+ * Chooses pages_per_split among the smallest values whose workgroups fit one,
+ * two, three or four rounds of `num_cus` compute units (0 = 256), by the
+ * shortest estimated duration when workgroup i waits for a free compute unit
+ * of XCD i % 8 (one workgroup per unit at a time) and costs its pages plus a
+ * fixed start-up of two pages.  Writes *pages_per_split >= 1 and *max_splits >= 1 (1 and 1 for an
+ * all-empty batch).  Returns MLA_ERR_NULL_PTR for a NULL output (or NULL
+ * seq_lens with B > 0), MLA_ERR_BAD_SHAPE for a negative length or a plan
+ * whose grid would exceed 2^31 - 1 workgroups.  Touches no device.
+ */
+int mla_decode_plan_lens(const int32_t* seq_lens, int B, int n_q, int H, int num_cus,
+                         int* pages_per_split, int* max_splits);
+
 /* Static text for a status code. */
 const char* mla_status_string(int status);
 

@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     mla_decode_paged,
     mla_decode_paged_append,
     mla_decode_plan,
+    mla_decode_plan_lens,
     status_string,
 )
 from .runner import DecodeStep  # noqa: F401

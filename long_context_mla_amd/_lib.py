@@ -52,15 +52,17 @@ def _load() -> ctypes.CDLL:
     lib.mla_decode_combine.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P]
     lib.mla_decode_paged_append.argtypes = [P, I, P, P, P, I, P, P, I, I, I, I, I, F, I, I, P, P, P, P, P]
     lib.mla_decode_plan.argtypes = [I, I, I, I, L, I, ctypes.POINTER(I), ctypes.POINTER(I)]
+    lib.mla_decode_plan_lens.argtypes = [P, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
     lib.mla_status_string.argtypes = [I]
     lib.mla_status_string.restype = ctypes.c_char_p
-    for fn in ("kv_append_fp8", "mla_decode_paged", "mla_decode_combine", "mla_decode_plan"):
+    for fn in ("kv_append_fp8", "mla_decode_paged", "mla_decode_paged_append", "mla_decode_combine",
+               "mla_decode_plan", "mla_decode_plan_lens"):
         getattr(lib, fn).restype = I
     return lib
 
 
 LIB = _load()
-EXPORTS = ("kv_append_fp8", "mla_decode_paged", "mla_decode_combine", "mla_decode_plan",
+EXPORTS = ("kv_append_fp8", "mla_decode_paged", "mla_decode_combine", "mla_decode_plan", "mla_decode_plan_lens",
            "mla_status_string")
 
 
@@ -237,6 +239,19 @@ def mla_decode_combine(o_partial, lse_partial, seq_lens, max_blocks, pages_per_s
     _check("mla_decode_combine", LIB.mla_decode_combine(
         _ptr(o_partial), _ptr(lse_partial), _ptr(seq_lens), B, n_q, H, int(max_blocks),
         int(pages_per_split), max_splits, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def mla_decode_plan_lens(seq_lens, n_q, H, num_cus=0):
+    """Host-only split plan from the batch's lengths (a host sequence of ints):
+    returns (pages_per_split, max_splits)."""
+    import numpy as np
+
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32).reshape(-1))
+    pps, ms = ctypes.c_int(0), ctypes.c_int(0)
+    _check("mla_decode_plan_lens", LIB.mla_decode_plan_lens(
+        lens.ctypes.data if lens.size else None, int(lens.size), int(n_q), int(H), int(num_cus),
+        ctypes.byref(pps), ctypes.byref(ms)))
+    return pps.value, ms.value
 
 
 def mla_decode_plan(B, n_q, H, max_seq_len, total_seq_len, num_cus=0):

@@ -115,3 +115,85 @@ def test_plan_rejects_bad_input():
         m.mla_decode_plan(1, 0, 64, 10, 10)
     with pytest.raises(m.MlaError):
         m.mla_decode_plan(1, 1, 64, -1, 10)
+
+
+def _model_makespan(lens, n_q, H, pps, cus, fixed=2):
+    """The planner's duration model written out: workgroups in 1-D launch order
+    (units b * max_splits + split round robin over 8 XCDs, row groups
+    consecutive), workgroup i on the first free compute unit of XCD i % 8,
+    costing a fixed start plus its pages."""
+    import heapq
+
+    pages = [-(-int(L) // 64) for L in lens]
+    ms = -(-max(pages) // pps)
+    n_rg = -(-(n_q * H) // 32)
+    B = len(lens)
+    grid = (B * ms + 7) // 8 * 8 * n_rg
+    pools = [[0] * max(1, cus // 8) for _ in range(8)]
+    end = 0
+    for i in range(grid):
+        u = (i >> 3) // n_rg * 8 + (i & 7)
+        if u >= B * ms:
+            continue
+        b, s = divmod(u, ms)
+        n = min(pages[b], s * pps + pps) - s * pps
+        if n <= 0 and s != 0:
+            continue
+        t = heapq.heappop(pools[i & 7]) + fixed + max(n, 0)
+        heapq.heappush(pools[i & 7], t)
+        end = max(end, t)
+    return end
+
+
+def _lens(kind):
+    import numpy as np
+
+    rng = np.random.default_rng(4)
+    if kind == "single":
+        return [100_001]
+    if kind == "uniform32":
+        return list(rng.integers(60_000, 140_000, 32))
+    if kind == "lognormal64":
+        x = np.clip(np.exp(rng.normal(np.log(16_000), 0.8, 64)), 1000, 128_000)
+        return list((x * 1.37e6 / x.sum()).astype(int))
+    if kind == "spec16":
+        return [142_004] * 16
+    if kind == "tiny":
+        return [0, 1, 63, 64, 65]
+    return [0, 0]
+
+
+@pytest.mark.parametrize("kind,n_q,H,cus", [
+    ("single", 1, 64, 256), ("uniform32", 1, 64, 256), ("lognormal64", 1, 64, 256),
+    ("spec16", 4, 64, 256), ("tiny", 2, 16, 80), ("empty", 1, 64, 256), ("lognormal64", 1, 64, 7),
+])
+def test_plan_lens(kind, n_q, H, cus):
+    """mla_decode_plan_lens covers every page with at most one short split per
+    request, fits its workgroups into at most four rounds when the requests
+    allow it, and (under its own duration model) never does worse than the
+    plan from the longest and summed lengths alone."""
+    import long_context_mla_amd as m
+
+    lens = _lens(kind)
+    pps, ms = m.mla_decode_plan_lens(lens, n_q, H, cus)
+    pages = [-(-int(L) // 64) for L in lens]
+    assert pps >= 1 and ms >= 1
+    if max(pages) == 0:
+        assert (pps, ms) == (1, 1)
+        return
+    assert pps * ms >= max(pages) and pps * (ms - 1) < max(pages)
+    n_rg = -(-(n_q * H) // 32)
+    wgs = sum(max(1, -(-p // pps)) for p in pages) * n_rg
+    if len(lens) * n_rg <= 4 * cus:
+        assert wgs <= 4 * cus
+    old = m.mla_decode_plan(len(lens), n_q, H, max(lens), sum(lens), cus)[0]
+    assert _model_makespan(lens, n_q, H, pps, cus) <= _model_makespan(lens, n_q, H, old, cus)
+
+
+def test_plan_lens_rejects_bad_input():
+    import long_context_mla_amd as m
+
+    with pytest.raises(m.MlaError):
+        m.mla_decode_plan_lens([10, -1], 1, 64)
+    with pytest.raises(m.MlaError):
+        m.mla_decode_plan_lens([10], 0, 64)
