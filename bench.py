@@ -79,10 +79,15 @@ def copy_probe(nbytes, steps):
     print(json.dumps({"copy_probe_bytes": nbytes, "launches": steps}), flush=True)
 
 
+# the sources the FP8 decode kernel is compiled from (host-side planning and
+# the other kernels do not change its traffic)
+KERNEL_SOURCES = ("mla_decode_fp8.hip", "decode_tile.h", "device_common.h", "launch.h")
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "long_context_mla_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in KERNEL_SOURCES:
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 

@@ -228,20 +228,23 @@ int mla_decode_plan_lens(const int32_t* seq_lens, int B, int n_q, int H, int num
     std::vector<MinHeap> free_at(8);
     for (auto& h : free_at)
       for (int c = 0; c < per_xcd; ++c) h.push(0);
-    const int64_t grid = mla::decode_grid_size(B, ms, n_rg);
+    // Unit u = b * ms + split is launched on XCD u % 8, the units of an XCD in
+    // increasing u (its n_rg workgroups back to back); units past a request's
+    // last page exit at once and are skipped.  The cost is linear in the
+    // number of working units, whatever the grid size.
     int64_t end = 0;
-    for (int64_t id = 0; id < grid; ++id) {
-      const int64_t u = (id >> 3) / n_rg * 8 + (id & 7);
-      if (u >= (int64_t)B * ms) continue;
-      const int b = (int)(u / ms), split = (int)(u % ms);
-      const int first = split * pps;
-      const int n = std::min(pages[b], first + pps) - first;
-      if (n <= 0 && split != 0) continue;  // exits at once
-      MinHeap& h = free_at[id & 7];
-      const int64_t t = h.top() + kFixedPages + std::max(n, 0);
-      h.pop();
-      h.push(t);
-      end = std::max(end, t);
+    for (int b = 0; b < B; ++b) {
+      const int n_units = std::max(1, (pages[b] + pps - 1) / pps);
+      for (int split = 0; split < n_units; ++split) {
+        const int n = std::max(0, std::min(pages[b], (split + 1) * pps) - split * pps);
+        MinHeap& h = free_at[((int64_t)b * ms + split) & 7];
+        for (int r = 0; r < n_rg; ++r) {
+          const int64_t t = h.top() + kFixedPages + n;
+          h.pop();
+          h.push(t);
+          end = std::max(end, t);
+        }
+      }
     }
     return end;
   };
