@@ -80,6 +80,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   const int p_begin = split * a.pps;
   const int64_t bt_row = (int64_t)b * a.max_blocks;
   constexpr int QBUF = T::NBUF - 1;
+  constexpr int kQueryLoads = 9;  // 16-byte query copies per score wave (32 rows x 1,152 B / 4 waves)
 
   // Before anything waits, the score waves issue the two loads that depend on
   // the launch arguments alone, so that their latencies overlap the length's:
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     const int rmax = a.R - 1 - r0;
     const uint32_t qlds = lds_addr(&s_kv[QBUF][0]);
 #pragma unroll
-    for (int j = 0; j < 9; ++j) {
+    for (int j = 0; j < kQueryLoads; ++j) {
       const int slot = (qw * 9 + j) * 64 + lane;  // 2304 slots = 32 rows x 72 chunks
       const int r = slot / 72;
       const int c = (slot - r * 72) ^ ((r >> 1) & 7);
@@ -158,9 +159,12 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     // Page ids of the split, 64 at a time, one per lane; picked out with
     // readlane so the DMA issue never waits on a scalar load.  Ids past the
     // split are never used; every used one is clamped to the pool.  The first
-    // chunk was requested at the start (it lands with the query copy); later
-    // chunks, and the first again on a restart, wait for themselves.
-    asm volatile("s_waitcnt vmcnt(0)" : "+v"(ids) :: "memory");
+    // chunk was requested at the start, before the wave's nine query copies:
+    // loads complete in order, so waiting until nine remain waits for the ids
+    // alone and the first pages' copies go out while the query still lands.
+    // Later chunks, and the first again on a restart, wait for themselves.
+    static_assert(kQueryLoads == 9, "the wait below counts the query copies");
+    asm volatile("s_waitcnt vmcnt(9)" : "+v"(ids) :: "memory");
     int id_chunk = 0;
     auto reload_ids = [&](int chunk) {
       id_chunk = chunk;
