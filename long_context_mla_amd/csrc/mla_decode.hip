@@ -173,10 +173,8 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
   // paired so that a lane's slots of k-blocks 2i and 2i+1 are the 16
   // consecutive dims of one 16-byte FP8 chunk of K (both cache types use
   // this order).  The wait covers the query only, not the pages behind it.
-  if (T::DIST == 2 && n_it >= 2)
-    wait_vmcnt<2 * LPP>();
-  else
-    wait_vmcnt<LPP>();
+  static_assert(T::DIST == 1, "one page copy is in flight behind the query");
+  wait_vmcnt<LPP>();
   __syncthreads();
   bf16x8 qop[2][kD / 32];
 #pragma unroll
