@@ -12,9 +12,11 @@ Modules
               (``partial_ref``), the log-sum-exp merge (``merge_ref``) and the
               FP8 cache append (``append_ref``), plus a pure-Python loop version
               of the attention (``decode_naive``) for tiny cases.
+``integrity`` the KV page-tag check (``check_pages_ref``): per-request status
+              bits and the lengths decode may use.
 
 Parity pins for every function live in ``tests/test_oracle_*.py``; none of the
 oracle's functions is left unpinned.
 """
 
-from . import e4m3, mla  # noqa: F401
+from . import e4m3, integrity, mla  # noqa: F401
