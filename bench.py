@@ -59,6 +59,8 @@ def parse():
                     help="kv_append_fp8 as its own launch before mla_decode_paged")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of one HIP graph per step")
+    ap.add_argument("--no-page-check", action="store_true",
+                    help="skip timing the KV page-tag check in front of the step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes --steps times (the "
                          "reference reading for HBM traffic counters) and exit")
@@ -145,6 +147,73 @@ def cpu_baseline(w, repeats, seconds):
                       f"median of {len(times)} runs of {t:.2f} s, {sum(times):.1f} s in all (fp64 numpy)"}
 
 
+def time_page_check(args, w, mla, torch, np, dev, stream, cap, step, bt, sl, run, graphs):
+    """The KV page-tag check (kv_check_pages) in front of the step: its kernel
+    alone (back to back inside one HIP graph), and the step's HIP graph with
+    and without it, replayed in alternating rounds (the median round of each)."""
+    rng = np.random.default_rng(77)
+    tags = rng.integers(0, 2**32, size=w.num_pages, dtype=np.uint64).astype(np.uint32)
+    bt_h = w.block_table
+    exp = np.where(bt_h >= 0, tags[np.clip(bt_h, 0, w.num_pages - 1)], 0).astype(np.uint32)
+    tags_t = torch.from_numpy(tags.view(np.int32)).to(dev)
+    exp_t = torch.from_numpy(exp.view(np.int32)).to(dev)
+    step.check(tags_t, bt, exp_t, sl, None, stream=stream)
+    torch.cuda.synchronize()
+    flagged = int((step.status != 0).sum().item())
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the kernel alone: one graph of 20 back-to-back checks (no host launch cost)
+    burst = torch.cuda.CUDAGraph()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(burst, stream=cap):
+            for _ in range(20):
+                step.check(tags_t, bt, exp_t, sl, None, stream=cap)
+    stream.wait_stream(cap)
+    burst.replay()
+    torch.cuda.synchronize()
+    reps = max(args.steps // 20, 5)
+    start.record(stream)
+    for _ in range(reps):
+        burst.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    k_us = start.elapsed_time(end) / (reps * 20) * 1000
+    checked = []
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        for k in range(args.rotate):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step.check(tags_t, bt, exp_t, sl, None, stream=cap)
+                run(k, st=cap, lens=step.checked_lens)
+            checked.append(g)
+    stream.wait_stream(cap)
+    for i in range(args.warmup):
+        checked[i % args.rotate].replay()
+    rounds = {"plain": [], "checked": []}
+    for _ in range(5):
+        for name, gs in (("plain", graphs), ("checked", checked)):
+            torch.cuda.synchronize()
+            start.record(stream)
+            for i in range(args.steps):
+                gs[i % args.rotate].replay()
+            end.record(stream)
+            torch.cuda.synchronize()
+            rounds[name].append(start.elapsed_time(end) / args.steps)
+    plain = float(np.median(rounds["plain"]))
+    with_check = float(np.median(rounds["checked"]))
+    pages = int(sum(-(-int(L) // 64) for L in w.seq_lens))
+    return {
+        "kernel": "kv_check_pages_kernel",
+        "kernel_us": round(k_us, 3),
+        "bytes": pages * 16 + w.B * 12,
+        "ms_per_step_graph_plain": round(plain, 5),
+        "ms_per_step_graph_checked": round(with_check, 5),
+        "overhead_frac": round(with_check / plain - 1.0, 4),
+        "flagged_requests": flagged,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -207,23 +276,24 @@ def main():
                           pages_per_split=pps, max_splits=ms, seq_lens_host=w.seq_lens)
     stream = torch.cuda.current_stream()
 
-    def run(i, ev=None, st=None):
+    def run(i, ev=None, st=None, lens=None):
         st = st or stream
+        sl_ = sl if lens is None else lens
         k = i % args.rotate
         fused = new_rows is not None and not args.separate_append
         if new_rows is not None and not fused:
-            mla.kv_append_fp8(new_rows, caches[k], scales[k], w.scale_mode, bt, sl, stream=st)
+            mla.kv_append_fp8(new_rows, caches[k], scales[k], w.scale_mode, bt, sl_, stream=st)
         if ev is not None:
             ev[0].record(st)
         if fused:
-            mla.mla_decode_paged_append(new_rows, q, caches[k], scales[k], w.scale_mode, bt, sl,
+            mla.mla_decode_paged_append(new_rows, q, caches[k], scales[k], w.scale_mode, bt, sl_,
                                         w.softmax_scale, step.pps, step.max_splits, step.o_partial,
                                         step.lse_partial, step.out, step.lse, stream=st)
         else:
-            step.decode(q, caches[k], scales[k], w.scale_mode, bt, sl, w.softmax_scale, stream=st)
+            step.decode(q, caches[k], scales[k], w.scale_mode, bt, sl_, w.softmax_scale, stream=st)
         if ev is not None:
             ev[1].record(st)
-        step.combine(sl, stream=st)
+        step.combine(sl_, stream=st)
 
     for i in range(args.warmup):
         run(i)
@@ -244,6 +314,7 @@ def main():
     k_us = float(k_ms.mean() * 1000)
     ms_step = ms_step_eager
     ms_step_graph = None
+    page_check = None
     # Pass 1b: the decode launches alone, back to back on the stream, between
     # one pair of events: the per-launch figure holds the kernel plus the
     # dispatch gap between two kernels, not the latency of an event record.
@@ -288,6 +359,9 @@ def main():
         # the step as a caller would launch it: the faster of the two forms,
         # both timed above over the same number of steps
         ms_step = min(ms_step_graph, ms_step_eager)
+        if not args.no_page_check:
+            page_check = time_page_check(args, w, mla, torch, np, dev, stream, cap, step, bt, sl, run,
+                                         graphs)
 
     tokens = w.total_tokens()
     unique = w.unique_tokens()
@@ -349,6 +423,8 @@ def main():
         "ms_per_step_eager": round(ms_step_eager, 5),
         "setup_s": round(t_setup, 1),
     }
+    if page_check is not None:
+        line["page_check"] = page_check
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_repeats, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -66,6 +66,15 @@ typedef enum {
   MLA_ERR_HIP = 4
 } mla_status_t;
 
+/* Per-request result bits of kv_check_pages (0 = the request may read the cache). */
+typedef enum {
+  MLA_PAGE_OK = 0,
+  MLA_PAGE_BAD_LEN = 1,      /* seq_lens[b] < 0 or > max_blocks * 64 */
+  MLA_PAGE_OUT_OF_RANGE = 2, /* a page-map entry it reads is outside [0, num_pages) */
+  MLA_PAGE_WRONG_PAGE = 4,   /* a page-map entry it reads differs from the recorded page */
+  MLA_PAGE_STALE_TAG = 8     /* a page it reads carries another tag than the recorded one */
+} mla_page_status_t;
+
 typedef enum { MLA_CACHE_BF16 = 0, MLA_CACHE_FP8_E4M3 = 1 } mla_cache_dtype_t;
 
 typedef enum {
@@ -196,6 +205,42 @@ int mla_decode_plan(int B, int n_q, int H, int max_seq_len, int64_t total_seq_le
  */
 int mla_decode_plan_lens(const int32_t* seq_lens, int B, int n_q, int H, int num_cus,
                          int* pages_per_split, int* max_splits);
+
+/*
+ * kv_check_pages — the KV page-tag integrity check, a batch launch of its own
+ * ahead of decode ("Smaller, faster, safer", section "Protecting a shared KV
+ * cache": every physical page carries a tag that changes whenever the page is
+ * handed out again; the server records the (page, tag) pairs each request
+ * expects; before decode reads the cache the records are compared with the
+ * current state, and a request that does not match is aborted).
+ *   page_tags       uint32 [num_pages], the current tag of each physical page.
+ *   block_table     int32 [B, max_blocks], the page map decode will read.
+ *   expected_pages  int32 [B, max_blocks], the recorded pages, or NULL to take
+ *                   the page map itself as the record.
+ *   expected_tags   uint32 [B, max_blocks], the recorded tag of each entry.
+ *   seq_lens        int32 [B].
+ *   status          int32 [B] out: or of mla_page_status_t bits.
+ *   checked_lens    int32 [B] out: seq_lens[b] where status[b] == 0, else 0.
+ *                   It may be seq_lens itself (the lengths are then masked in
+ *                   place); it must not overlap status or the other inputs.
+ * Request b reads logical pages j < ceil(L / 64), L = seq_lens[b]; only those
+ * entries are checked.  Per entry: the page-map entry against the recorded
+ * page (MLA_PAGE_WRONG_PAGE), the entry against [0, num_pages)
+ * (MLA_PAGE_OUT_OF_RANGE, and then no tag is read), else the page's current
+ * tag against the recorded tag (MLA_PAGE_STALE_TAG).  A length outside
+ * [0, max_blocks * 64] gives MLA_PAGE_BAD_LEN alone.  Passing checked_lens as
+ * the seq_lens of kv_append_fp8, mla_decode_paged(_append) and
+ * mla_decode_combine aborts the flagged requests within the step: none of
+ * their pages is read or written, their output rows are 0 and their
+ * log-sum-exp is -inf.  One workgroup of 1024 threads per request.
+ * Returns MLA_ERR_BAD_SHAPE for B < 0, num_pages < 1, max_blocks < 1 or
+ * max_blocks * 64 >= 2^31; MLA_ERR_NULL_PTR for a NULL required pointer with
+ * B > 0; nothing is launched for B == 0.
+ */
+int kv_check_pages(const uint32_t* page_tags, int num_pages, const int32_t* block_table,
+                   const int32_t* expected_pages, const uint32_t* expected_tags,
+                   const int32_t* seq_lens, int B, int max_blocks, int32_t* status,
+                   int32_t* checked_lens, void* stream);
 
 /* Static text for a status code. */
 const char* mla_status_string(int status);

@@ -10,10 +10,16 @@ from ._lib import (  # noqa: F401
     CACHE_FP8_E4M3,
     LIB_PATH,
     MlaError,
+    PAGE_BAD_LEN,
+    PAGE_OK,
+    PAGE_OUT_OF_RANGE,
+    PAGE_STALE_TAG,
+    PAGE_WRONG_PAGE,
     SCALE_NONE,
     SCALE_PER_TENSOR,
     SCALE_PER_TOKEN,
     kv_append_fp8,
+    kv_check_pages,
     mla_decode_combine,
     mla_decode_paged,
     mla_decode_paged_append,

@@ -53,17 +53,24 @@ def _load() -> ctypes.CDLL:
     lib.mla_decode_paged_append.argtypes = [P, I, P, P, P, I, P, P, I, I, I, I, I, F, I, I, P, P, P, P, P]
     lib.mla_decode_plan.argtypes = [I, I, I, I, L, I, ctypes.POINTER(I), ctypes.POINTER(I)]
     lib.mla_decode_plan_lens.argtypes = [P, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
+    lib.kv_check_pages.argtypes = [P, I, P, P, P, P, I, I, P, P, P]
     lib.mla_status_string.argtypes = [I]
     lib.mla_status_string.restype = ctypes.c_char_p
     for fn in ("kv_append_fp8", "mla_decode_paged", "mla_decode_paged_append", "mla_decode_combine",
-               "mla_decode_plan", "mla_decode_plan_lens"):
+               "mla_decode_plan", "mla_decode_plan_lens", "kv_check_pages"):
         getattr(lib, fn).restype = I
     return lib
 
 
 LIB = _load()
-EXPORTS = ("kv_append_fp8", "mla_decode_paged", "mla_decode_combine", "mla_decode_plan", "mla_decode_plan_lens",
-           "mla_status_string")
+EXPORTS = ("kv_append_fp8", "mla_decode_paged", "mla_decode_paged_append", "mla_decode_combine",
+           "mla_decode_plan", "mla_decode_plan_lens", "kv_check_pages", "mla_status_string")
+
+PAGE_OK = 0
+PAGE_BAD_LEN = 1
+PAGE_OUT_OF_RANGE = 2
+PAGE_WRONG_PAGE = 4
+PAGE_STALE_TAG = 8
 
 
 def status_string(status: int) -> str:
@@ -261,3 +268,38 @@ def mla_decode_plan(B, n_q, H, max_seq_len, total_seq_len, num_cus=0):
                                                   int(total_seq_len), int(num_cus),
                                                   ctypes.byref(pps), ctypes.byref(ms)))
     return pps.value, ms.value
+
+
+def _need_tags(t, name, device, ndim):
+    if not isinstance(t, torch.Tensor) or t.dtype not in (torch.int32, torch.uint32):
+        raise TypeError(f"{name} must be an int32 or uint32 tensor (the tag bits)")
+    _need(t, name, t.dtype, device, ndim)
+
+
+def kv_check_pages(page_tags, block_table, expected_tags, seq_lens, status, checked_lens,
+                   expected_pages=None, stream=None):
+    """page_tags [num_pages] and expected_tags [B, max_blocks] (uint32 or int32 bits);
+    block_table, expected_pages (or None) int32 [B, max_blocks]; seq_lens int32 [B];
+    writes status int32 [B] (PAGE_* bits) and checked_lens int32 [B] (may be seq_lens)."""
+    dev = block_table.device
+    _need_tags(page_tags, "page_tags", dev, 1)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need_tags(expected_tags, "expected_tags", dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    _need(status, "status", torch.int32, dev, 1)
+    _need(checked_lens, "checked_lens", torch.int32, dev, 1)
+    B, max_blocks = block_table.shape
+    if expected_pages is not None:
+        _need(expected_pages, "expected_pages", torch.int32, dev, 2)
+        if tuple(expected_pages.shape) != (B, max_blocks):
+            raise ValueError("expected_pages must match block_table's shape")
+    if tuple(expected_tags.shape) != (B, max_blocks):
+        raise ValueError("expected_tags must match block_table's shape")
+    if seq_lens.shape[0] != B or status.shape[0] != B or checked_lens.shape[0] != B:
+        raise ValueError("seq_lens / status / checked_lens must have B entries")
+    if B and status.data_ptr() in (checked_lens.data_ptr(), seq_lens.data_ptr()):
+        raise ValueError("status must not share memory with seq_lens or checked_lens")
+    _check("kv_check_pages", LIB.kv_check_pages(
+        _ptr(page_tags), page_tags.shape[0], _ptr(block_table), _ptr(expected_pages),
+        _ptr(expected_tags), _ptr(seq_lens), B, max_blocks, _ptr(status), _ptr(checked_lens),
+        _stream(stream)))

@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_decode.so")
-SOURCES = ["api.hip", "kv_append.hip", "mla_decode.hip", "mla_decode_fp8.hip", "mla_combine.hip"]
+SOURCES = ["api.hip", "kv_append.hip", "mla_decode.hip", "mla_decode_fp8.hip", "mla_combine.hip", "kv_check.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

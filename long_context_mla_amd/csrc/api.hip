@@ -115,6 +115,30 @@ int kv_append_fp8(const void* kv_new, void* kv_cache, float* kv_scale, int scale
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+int kv_check_pages(const uint32_t* page_tags, int num_pages, const int32_t* block_table,
+                   const int32_t* expected_pages, const uint32_t* expected_tags,
+                   const int32_t* seq_lens, int B, int max_blocks, int32_t* status,
+                   int32_t* checked_lens, void* stream) {
+  if (B < 0 || max_blocks < 1 || num_pages < 1) return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)max_blocks * MLA_PAGE_SIZE > 2147483647LL) return MLA_ERR_BAD_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!page_tags || !block_table || !expected_tags || !seq_lens || !status || !checked_lens)
+    return MLA_ERR_NULL_PTR;
+  mla::CheckArgs a;
+  a.page_tags = page_tags;
+  a.block_table = block_table;
+  a.expected_pages = expected_pages ? expected_pages : block_table;  // no record: the map is the record
+  a.expected_tags = expected_tags;
+  a.seq_lens = seq_lens;
+  a.status = status;
+  a.checked_lens = checked_lens;
+  a.B = B;
+  a.max_blocks = max_blocks;
+  a.num_pages = num_pages;
+  const hipError_t e = mla::launch_kv_check(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 int mla_decode_paged(const void* q, const void* kv_cache, int cache_dtype, const float* kv_scale,
                      int scale_mode, const int32_t* block_table, const int32_t* seq_lens, int B,
                      int n_q, int H, int max_blocks, int num_pages, float softmax_scale,

@@ -16,6 +16,17 @@ struct AppendArgs {
   int B, n_new, max_blocks, num_pages;
 };
 
+struct CheckArgs {
+  const uint32_t* page_tags;       // [num_pages] current tag of each physical page
+  const int32_t* block_table;      // [B, max_blocks] page map decode will read
+  const int32_t* expected_pages;   // [B, max_blocks] recorded pages (block_table when none are kept)
+  const uint32_t* expected_tags;   // [B, max_blocks] recorded tags
+  const int32_t* seq_lens;         // [B]
+  int32_t* status;                 // [B] written
+  int32_t* checked_lens;           // [B] written; may be seq_lens
+  int B, max_blocks, num_pages;
+};
+
 struct DecodeArgs {
   const uint16_t* q;        // bf16 [B, R, 576], R = n_q * H
   const uint8_t* cache;     // e4m3 or bf16 rows [num_pages, 64, 576]
@@ -59,5 +70,6 @@ hipError_t launch_kv_append(const AppendArgs& a, int scale_mode, hipStream_t str
 hipError_t launch_decode(const DecodeArgs& a, int cache_kind, int scale_mode, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeArgs& a, int scale_mode, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_kv_check(const CheckArgs& a, hipStream_t stream);
 
 }  // namespace mla

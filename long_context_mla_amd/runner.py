@@ -2,7 +2,10 @@
 cache), split-KV attention, then the split merge, on the current stream with
 buffers allocated once per batch shape.  On an FP8 cache the append rides in
 the decode launch (mla_decode_paged_append); fuse_append=False issues
-kv_append_fp8 and mla_decode_paged separately."""
+kv_append_fp8 and mla_decode_paged separately.  With ``page_check`` the step
+starts with the KV page-tag check (kv_check_pages) and runs on the lengths it
+returns, so a request whose pages fail the check reads and writes no page and
+gets zero output rows (``status`` holds its reason)."""
 
 from __future__ import annotations
 
@@ -35,6 +38,7 @@ class DecodeStep:
                                            device=device)
         else:
             self.o_partial = self.lse_partial = None
+        self.status = self.checked_lens = None
 
     def decode(self, q, kv_cache, kv_scale, scale_mode, block_table, seq_lens, softmax_scale,
                stream=None):
@@ -47,8 +51,22 @@ class DecodeStep:
             _lib.mla_decode_combine(self.o_partial, self.lse_partial, seq_lens, self.max_blocks,
                                     self.pps, self.out, self.lse, stream=stream)
 
+    def check(self, page_tags, block_table, expected_tags, seq_lens, expected_pages=None, stream=None):
+        """kv_check_pages into this step's status / checked_lens; returns checked_lens."""
+        if self.status is None:
+            self.status = torch.empty(self.B, dtype=torch.int32, device=block_table.device)
+            self.checked_lens = torch.empty(self.B, dtype=torch.int32, device=block_table.device)
+        _lib.kv_check_pages(page_tags, block_table, expected_tags, seq_lens, self.status,
+                            self.checked_lens, expected_pages, stream=stream)
+        return self.checked_lens
+
     def __call__(self, q, kv_cache, kv_scale, scale_mode, block_table, seq_lens, softmax_scale,
-                 new_rows=None, stream=None):
+                 new_rows=None, stream=None, page_check=None):
+        """page_check: (page_tags, expected_tags, expected_pages or None) to run the
+        page-tag check first."""
+        if page_check is not None:
+            page_tags, expected_tags, expected_pages = page_check
+            seq_lens = self.check(page_tags, block_table, expected_tags, seq_lens, expected_pages, stream)
         if new_rows is not None and new_rows.shape[1] > 0:
             if self.fuse_append:
                 _lib.mla_decode_paged_append(new_rows, q, kv_cache, kv_scale, scale_mode, block_table,

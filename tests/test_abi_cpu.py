@@ -84,6 +84,27 @@ def test_append_and_combine_validation(lib):
     assert lib.mla_status_string(3) == b"unsupported configuration"
 
 
+def test_page_check_validation(lib):
+    P = ctypes.c_void_p
+    ok = dict(tags=1, np_=10, bt=1, ep=None, et=1, sl=1, B=2, mb=4, st=1, cl=1)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        Q = lambda v: None if v is None else P(v)  # noqa: E731
+        return lib.kv_check_pages(Q(a["tags"]), a["np_"], Q(a["bt"]), Q(a["ep"]), Q(a["et"]), Q(a["sl"]),
+                                  a["B"], a["mb"], Q(a["st"]), Q(a["cl"]), None)
+
+    assert call(tags=None) == 1
+    assert call(et=None) == 1
+    assert call(st=None) == 1
+    assert call(cl=None) == 1
+    assert call(B=-1) == 2
+    assert call(np_=0) == 2
+    assert call(mb=0) == 2
+    assert call(mb=2**25) == 2  # 64 * max_blocks must fit an int32
+    assert call(B=0, tags=None, bt=None, et=None, sl=None, st=None, cl=None) == 0
+
+
 @pytest.mark.parametrize("B,n_q,H,maxL,total,cus", [
     (1, 1, 64, 100_001, 100_001, 256),
     (32, 1, 64, 137_661, 3_269_170, 256),

@@ -1,0 +1,144 @@
+"""GPU parity of the KV page-tag check (kv_check_pages) with the oracle, bit for
+bit, on allocator histories with planted faults; and the check in front of a
+decode step: a flagged request reads and writes no page and gets zero rows,
+the others still match the attention oracle.  All calls go through the C ABI."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import integrity as oi
+from synth import integrity as si
+
+from _gpu import GpuState, bf16_tensor_to_f64, compare, log, oracle_decode
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_tag_check_small.json")
+
+
+def _dev(a, dtype=np.int32):
+    return torch.from_numpy(np.ascontiguousarray(a).view(dtype)).to("cuda:0")
+
+
+def _gpu_check(tags, bt, et, lens, ep=None, in_place=False):
+    import long_context_mla_amd as mla
+
+    B = bt.shape[0]
+    t_lens = _dev(lens)
+    status = torch.full((B,), -7, dtype=torch.int32, device="cuda:0")
+    checked = t_lens if in_place else torch.full((B,), -7, dtype=torch.int32, device="cuda:0")
+    mla.kv_check_pages(_dev(tags), _dev(bt), _dev(et), t_lens, status, checked,
+                       None if ep is None else _dev(ep))
+    torch.cuda.synchronize()
+    return status.cpu().numpy(), checked.cpu().numpy()
+
+
+def _assert_same(case, tag):
+    for ep in (case.expected_pages, None):
+        for in_place in (False, True):
+            want_s, want_l = oi.check_pages_ref(case.page_tags, case.block_table, case.expected_tags,
+                                                case.seq_lens, ep)
+            got_s, got_l = _gpu_check(case.page_tags, case.block_table, case.expected_tags, case.seq_lens,
+                                      ep, in_place)
+            log(f"{tag} record={'pages' if ep is not None else 'map'} in_place={in_place} "
+                f"flagged={int((want_s != 0).sum())}/{want_s.size}")
+            assert np.array_equal(got_s, want_s), (tag, np.nonzero(got_s != want_s))
+            assert np.array_equal(got_l, want_l), (tag, np.nonzero(got_l != want_l))
+
+
+def test_hand_worked_case():
+    with open(GOLDEN) as f:
+        g = json.load(f)
+    case = si.TagCase(np.asarray(g["page_tags"], np.uint32), np.asarray(g["block_table"], np.int32),
+                      np.asarray(g["expected_pages"], np.int32), np.asarray(g["expected_tags"], np.uint32),
+                      np.asarray(g["seq_lens"], np.int32))
+    got_s, got_l = _gpu_check(case.page_tags, case.block_table, case.expected_tags, case.seq_lens,
+                              case.expected_pages)
+    assert got_s.tolist() == g["status"] and got_l.tolist() == g["checked_lens"]
+    _assert_same(case, "golden")
+
+
+KINDS = ["stale", "wrong", "oob", "neg", "len", "neglen", "tail"]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_batch_with_planted_faults(seed):
+    rng = np.random.default_rng(1000 + seed)
+    B, mb = 64, 300
+    lens = [int(x) for x in rng.integers(0, mb * 64 + 1, size=B)]
+    lens[:6] = [0, 1, 64, 65, mb * 64, mb * 64 - 1]
+    faults = []
+    for _ in range(16):
+        b = int(rng.integers(0, B))
+        n = (lens[b] + 63) // 64
+        kind = KINDS[int(rng.integers(0, len(KINDS)))]
+        if kind in ("stale", "wrong", "oob", "neg") and n == 0:
+            continue
+        if kind == "tail" and n >= mb:
+            continue
+        j = int(rng.integers(0, n)) if kind != "tail" else int(rng.integers(n, mb))
+        faults.append((kind, b, j))
+    need = sum((x + 63) // 64 for x in lens)
+    c = si.make_case(seed, lens, mb, num_pages=need + 700, faults=faults, churn=100)
+    _assert_same(c, f"batch seed={seed} faults={len(faults)}")
+
+
+def test_long_requests_take_several_passes():
+    """Requests of more than 4096 pages: faults in the first and the second
+    pass of the workgroup, at the last page and exactly at page 4096."""
+    mb = 5000
+    lens = [mb * 64 - 3, 4097 * 64, 4096 * 64 + 1, 4096 * 64, mb * 64]
+    faults = [("stale", 0, 4999), ("wrong", 1, 4096), ("oob", 2, 4096), ("tail", 3, 4096)]
+    c = si.make_case(11, lens, mb, num_pages=sum((x + 63) // 64 for x in lens) + 100, faults=faults)
+    _assert_same(c, "long")
+
+
+def test_empty_batch_launches_nothing():
+    import long_context_mla_amd as mla
+
+    e = torch.empty((0,), dtype=torch.int32, device="cuda:0")
+    mla.kv_check_pages(torch.zeros(4, dtype=torch.int32, device="cuda:0"),
+                       torch.empty((0, 3), dtype=torch.int32, device="cuda:0"),
+                       torch.empty((0, 3), dtype=torch.int32, device="cuda:0"), e, e.clone(), e.clone())
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("fuse_append", [True, False])
+def test_flagged_request_is_aborted_within_the_step(fuse_append):
+    import long_context_mla_amd as mla
+
+    w = synth.custom("check_e2e", B=4, n_q=1, H=64, context_lens=(300, 200, 1000, 65), cache_dtype="fp8",
+                     scale_mode="token", seed=5)
+    rng = np.random.default_rng(9)
+    tags = rng.integers(0, 2**32, size=w.num_pages, dtype=np.uint64).astype(np.uint32)
+    bt = w.block_table
+    et = np.where(bt >= 0, tags[np.clip(bt, 0, w.num_pages - 1)], 0).astype(np.uint32)
+    victim = 1
+    last = (int(w.seq_lens[victim]) - 1) // 64  # the page the victim's new row goes to
+    page = int(bt[victim, last])
+    tags[page] ^= np.uint32(1)  # the page was handed out again
+    want_s, want_l = oi.check_pages_ref(tags, bt, et, w.seq_lens)
+    log(f"e2e fuse_append={fuse_append} L={w.seq_lens.tolist()} status={want_s.tolist()}")
+    assert want_s.tolist() == [0, oi.STALE_TAG, 0, 0]
+
+    g = GpuState(w)
+    before = g.cache[page].clone()
+    st = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(), g.device,
+                        fuse_append=fuse_append, seq_lens_host=w.seq_lens)
+    out, lse = st(g.q, g.cache, g.kv_scale, g.scale_mode, g.block_table, g.seq_lens, w.softmax_scale,
+                  new_rows=g.new_rows, page_check=(_dev(tags), _dev(et), None))
+    torch.cuda.synchronize()
+    assert st.status.cpu().numpy().tolist() == want_s.tolist()
+    assert st.checked_lens.cpu().numpy().tolist() == want_l.tolist()
+    o = bf16_tensor_to_f64(out)
+    l = lse.detach().cpu().double().numpy()
+    assert not o[victim].any() and np.all(np.isneginf(l[victim]))
+    assert torch.equal(g.cache[page], before), "an aborted request wrote into the cache"
+    keep = [0, 2, 3]
+    ref_o, ref_l = oracle_decode(w, requests=keep)
+    compare(o, l, ref_o, ref_l, requests=keep, tag=f"e2e fuse_append={fuse_append}")
