@@ -147,10 +147,12 @@ def cpu_baseline(w, repeats, seconds):
                       f"median of {len(times)} runs of {t:.2f} s, {sum(times):.1f} s in all (fp64 numpy)"}
 
 
-def time_page_check(args, w, mla, torch, np, dev, stream, cap, step, bt, sl, run, graphs):
-    """The KV page-tag check (kv_check_pages) in front of the step: its kernel
-    alone (back to back inside one HIP graph), and the step's HIP graph with
-    and without it, replayed in alternating rounds (the median round of each)."""
+def time_page_check(args, w, mla, torch, np, dev, stream, cap, step, bt, sl, run_checked, graphs):
+    """The KV page-tag check (kv_check_pages): its kernel alone (back to back
+    inside one HIP graph), and the step's HIP graph without it, with it in front
+    of the decode, and with it beside the decode on a second stream (the append
+    on the checked lengths after it, the combine masking flagged requests),
+    replayed in alternating rounds (the median round of each)."""
     rng = np.random.default_rng(77)
     tags = rng.integers(0, 2**32, size=w.num_pages, dtype=np.uint64).astype(np.uint32)
     bt_h = w.block_table
@@ -178,21 +180,26 @@ def time_page_check(args, w, mla, torch, np, dev, stream, cap, step, bt, sl, run
     end.record(stream)
     torch.cuda.synchronize()
     k_us = start.elapsed_time(end) / (reps * 20) * 1000
-    checked = []
-    cap.wait_stream(stream)
-    with torch.cuda.stream(cap):
-        for k in range(args.rotate):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
-                step.check(tags_t, bt, exp_t, sl, None, stream=cap)
-                run(k, st=cap, lens=step.checked_lens)
-            checked.append(g)
-    stream.wait_stream(cap)
-    for i in range(args.warmup):
-        checked[i % args.rotate].replay()
-    rounds = {"plain": [], "checked": []}
+    graphs_by_mode = {"plain": graphs}
+    for mode, overlap in (("sequential", False), ("overlapped", True)):
+        step.overlap_check = overlap
+        gs = []
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            for k in range(args.rotate):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    run_checked(k, cap, (tags_t, exp_t, None))
+                gs.append(g)
+        stream.wait_stream(cap)
+        graphs_by_mode[mode] = gs
+    step.overlap_check = False
+    for gs in graphs_by_mode.values():
+        for i in range(args.warmup):
+            gs[i % args.rotate].replay()
+    rounds = {m: [] for m in graphs_by_mode}
     for _ in range(5):
-        for name, gs in (("plain", graphs), ("checked", checked)):
+        for name, gs in graphs_by_mode.items():
             torch.cuda.synchronize()
             start.record(stream)
             for i in range(args.steps):
@@ -200,16 +207,19 @@ def time_page_check(args, w, mla, torch, np, dev, stream, cap, step, bt, sl, run
             end.record(stream)
             torch.cuda.synchronize()
             rounds[name].append(start.elapsed_time(end) / args.steps)
-    plain = float(np.median(rounds["plain"]))
-    with_check = float(np.median(rounds["checked"]))
+    med = {m: float(np.median(v)) for m, v in rounds.items()}
+    torch.cuda.synchronize()
+    flagged = max(flagged, int((step.status != 0).sum().item()))
     pages = int(sum(-(-int(L) // 64) for L in w.seq_lens))
     return {
         "kernel": "kv_check_pages_kernel",
         "kernel_us": round(k_us, 3),
         "bytes": pages * 16 + w.B * 12,
-        "ms_per_step_graph_plain": round(plain, 5),
-        "ms_per_step_graph_checked": round(with_check, 5),
-        "overhead_frac": round(with_check / plain - 1.0, 4),
+        "ms_per_step_graph_plain": round(med["plain"], 5),
+        "ms_per_step_graph_check_first": round(med["sequential"], 5),
+        "ms_per_step_graph_check_beside": round(med["overlapped"], 5),
+        "overhead_frac": round(med["sequential"] / med["plain"] - 1.0, 4),
+        "overhead_frac_check_beside": round(med["overlapped"] / med["plain"] - 1.0, 4),
         "flagged_requests": flagged,
     }
 
@@ -360,8 +370,13 @@ def main():
         # both timed above over the same number of steps
         ms_step = min(ms_step_graph, ms_step_eager)
         if not args.no_page_check:
-            page_check = time_page_check(args, w, mla, torch, np, dev, stream, cap, step, bt, sl, run,
-                                         graphs)
+            def run_checked(i, st, check):
+                k = i % args.rotate
+                step(q, caches[k], scales[k], w.scale_mode, bt, sl, w.softmax_scale, new_rows=new_rows,
+                     stream=st, page_check=check)
+
+            page_check = time_page_check(args, w, mla, torch, np, dev, stream, cap, step, bt, sl,
+                                         run_checked, graphs)
 
     tokens = w.total_tokens()
     unique = w.unique_tokens()

@@ -159,12 +159,22 @@ int mla_decode_paged(const void* q, const void* kv_cache, int cache_dtype, const
  * mla_decode_paged on that cache.  A row whose position has no visible page
  * (seq_lens[b] - n_new + j < 0) is skipped, as in kv_append_fp8.  Errors as in
  * the two calls it replaces; MLA_ERR_UNSUPPORTED for MLA_SCALE_NONE.
+ *
+ *   store_rows      1: as above.  0: the new rows take part in this launch's
+ *                   attention but nothing is written to kv_cache / kv_scale;
+ *                   the caller stores them with kv_append_fp8 (for instance on
+ *                   another stream, after kv_check_pages, with the checked
+ *                   lengths).  That append may run while this launch runs:
+ *                   the launch puts its own encoding over whatever it reads
+ *                   of the new rows' slots, so its results do not depend on
+ *                   when the append lands.
  */
 int mla_decode_paged_append(const void* kv_new, int n_new, const void* q, void* kv_cache,
                             float* kv_scale, int scale_mode, const int32_t* block_table,
                             const int32_t* seq_lens, int B, int n_q, int H, int max_blocks,
                             int num_pages, float softmax_scale, int pages_per_split, int max_splits,
-                            void* o_partial, float* lse_partial, void* out, float* lse, void* stream);
+                            void* o_partial, float* lse_partial, void* out, float* lse, int store_rows,
+                            void* stream);
 
 /*
  * mla_decode_combine — merge the split partials of mla_decode_paged
@@ -176,10 +186,17 @@ int mla_decode_paged_append(const void* kv_new, int n_new, const void* q, void* 
  * out = bf16(sum_s w_s o_s / sum_s w_s); lse = M + ln(sum_s w_s).
  * Same shapes as mla_decode_paged; pages_per_split and max_splits must be the
  * values that call used.
+ *   status     int32 [B] from kv_check_pages, or NULL.  A request whose entry
+ *              is non-zero merges no split: its rows get out = 0 and
+ *              lse = -inf, whatever its partials hold.  This lets the page
+ *              check run beside the decode launch (which then reads the
+ *              unchecked lengths; page ids are clamped, so a bad page map
+ *              still reads only inside the cache) and still keep a flagged
+ *              request from returning data read from another page.
  */
 int mla_decode_combine(const void* o_partial, const float* lse_partial, const int32_t* seq_lens,
                        int B, int n_q, int H, int max_blocks, int pages_per_split, int max_splits,
-                       void* out, float* lse, void* stream);
+                       void* out, float* lse, const int32_t* status, void* stream);
 
 /*
  * mla_decode_plan — host-only helper that picks pages_per_split and max_splits

@@ -49,8 +49,8 @@ def _load() -> ctypes.CDLL:
     P, I, F, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
     lib.kv_append_fp8.argtypes = [P, P, P, I, P, P, I, I, I, I, P]
     lib.mla_decode_paged.argtypes = [P, P, I, P, I, P, P, I, I, I, I, I, F, I, I, P, P, P, P, P]
-    lib.mla_decode_combine.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P]
-    lib.mla_decode_paged_append.argtypes = [P, I, P, P, P, I, P, P, I, I, I, I, I, F, I, I, P, P, P, P, P]
+    lib.mla_decode_combine.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P]
+    lib.mla_decode_paged_append.argtypes = [P, I, P, P, P, I, P, P, I, I, I, I, I, F, I, I, P, P, P, P, I, P]
     lib.mla_decode_plan.argtypes = [I, I, I, I, L, I, ctypes.POINTER(I), ctypes.POINTER(I)]
     lib.mla_decode_plan_lens.argtypes = [P, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
     lib.kv_check_pages.argtypes = [P, I, P, P, P, P, I, I, P, P, P]
@@ -184,9 +184,10 @@ def mla_decode_paged(q, kv_cache, kv_scale, scale_mode, block_table, seq_lens, s
 
 def mla_decode_paged_append(kv_new, q, kv_cache, kv_scale, scale_mode, block_table, seq_lens,
                             softmax_scale, pages_per_split, max_splits, o_partial=None,
-                            lse_partial=None, out=None, lse=None, stream=None):
+                            lse_partial=None, out=None, lse=None, stream=None, store_rows=True):
     """kv_append_fp8 then mla_decode_paged in one launch (E4M3 cache); kv_new bf16
-    [B, n_new, 576] (n_new may be 0); the other arguments as in those two."""
+    [B, n_new, 576] (n_new may be 0); the other arguments as in those two.
+    store_rows=False: the new rows serve this launch only (the caller stores them)."""
     mode = _SCALE_NAMES[scale_mode] if isinstance(scale_mode, str) else int(scale_mode)
     dev = q.device
     _need(q, "q", torch.bfloat16, dev, 4)
@@ -226,12 +227,13 @@ def mla_decode_paged_append(kv_new, q, kv_cache, kv_scale, scale_mode, block_tab
         float(softmax_scale), int(pages_per_split), int(max_splits),
         _ptr(o_partial) if max_splits > 1 else None, _ptr(lse_partial) if max_splits > 1 else None,
         _ptr(out) if max_splits == 1 else None, _ptr(lse) if max_splits == 1 else None,
-        _stream(stream)))
+        1 if store_rows else 0, _stream(stream)))
 
 
 def mla_decode_combine(o_partial, lse_partial, seq_lens, max_blocks, pages_per_split, out, lse,
-                       stream=None):
-    """Merge the partials of mla_decode_paged into out bf16 [B, n_q, H, 512] and lse fp32 [B, n_q, H]."""
+                       stream=None, status=None):
+    """Merge the partials of mla_decode_paged into out bf16 [B, n_q, H, 512] and lse fp32 [B, n_q, H];
+    status int32 [B] (kv_check_pages) or None: flagged requests get 0 / -inf rows."""
     dev = o_partial.device
     _need(o_partial, "o_partial", torch.bfloat16, dev, 5)
     _need(lse_partial, "lse_partial", torch.float32, dev, 4)
@@ -243,9 +245,13 @@ def mla_decode_combine(o_partial, lse_partial, seq_lens, max_blocks, pages_per_s
         raise ValueError("partial shape mismatch")
     if tuple(out.shape) != (B, n_q, H, VALUE_DIM) or tuple(lse.shape) != (B, n_q, H):
         raise ValueError("out / lse shape mismatch")
+    if status is not None:
+        _need(status, "status", torch.int32, dev, 1)
+        if status.shape[0] != B:
+            raise ValueError("status must have B entries")
     _check("mla_decode_combine", LIB.mla_decode_combine(
         _ptr(o_partial), _ptr(lse_partial), _ptr(seq_lens), B, n_q, H, int(max_blocks),
-        int(pages_per_split), max_splits, _ptr(out), _ptr(lse), _stream(stream)))
+        int(pages_per_split), max_splits, _ptr(out), _ptr(lse), _ptr(status), _stream(stream)))
 
 
 def mla_decode_plan_lens(seq_lens, n_q, H, num_cus=0):

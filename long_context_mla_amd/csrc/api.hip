@@ -33,7 +33,7 @@ int decode_impl(const void* q, const void* kv_cache, int cache_dtype, const floa
                 int scale_mode, const int32_t* block_table, const int32_t* seq_lens, int B, int n_q,
                 int H, int max_blocks, int num_pages, float softmax_scale, int pages_per_split,
                 int max_splits, void* o_partial, float* lse_partial, void* out, float* lse,
-                const void* kv_new, int n_new, void* stream) {
+                const void* kv_new, int n_new, int store_rows, void* stream) {
   if (int s = check_cache_mode(cache_dtype, scale_mode)) return s;
   if (bad_stream_free_shape(B, n_q, H)) return MLA_ERR_BAD_SHAPE;
   if (max_blocks < 1 || num_pages < 1 || pages_per_split < 1 || max_splits < 1) return MLA_ERR_BAD_SHAPE;
@@ -72,6 +72,7 @@ int decode_impl(const void* q, const void* kv_cache, int cache_dtype, const floa
   a.n_new = n_new;
   a.cache_out = static_cast<uint8_t*>(const_cast<void*>(kv_cache));
   a.scale_out = const_cast<float*>(kv_scale);
+  a.store_rows = store_rows ? 1 : 0;
   const int kind = cache_dtype == MLA_CACHE_FP8_E4M3 ? mla::kFp8 : mla::kBf16;
   const hipError_t e = mla::launch_decode(a, kind, scale_mode, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
@@ -146,25 +147,27 @@ int mla_decode_paged(const void* q, const void* kv_cache, int cache_dtype, const
                      void* out, float* lse, void* stream) {
   return decode_impl(q, kv_cache, cache_dtype, kv_scale, scale_mode, block_table, seq_lens, B, n_q, H,
                      max_blocks, num_pages, softmax_scale, pages_per_split, max_splits, o_partial,
-                     lse_partial, out, lse, nullptr, 0, stream);
+                     lse_partial, out, lse, nullptr, 0, 1, stream);
 }
 
 int mla_decode_paged_append(const void* kv_new, int n_new, const void* q, void* kv_cache,
                             float* kv_scale, int scale_mode, const int32_t* block_table,
                             const int32_t* seq_lens, int B, int n_q, int H, int max_blocks,
                             int num_pages, float softmax_scale, int pages_per_split, int max_splits,
-                            void* o_partial, float* lse_partial, void* out, float* lse, void* stream) {
+                            void* o_partial, float* lse_partial, void* out, float* lse, int store_rows,
+                            void* stream) {
   if (scale_mode != MLA_SCALE_PER_TENSOR && scale_mode != MLA_SCALE_PER_TOKEN) return MLA_ERR_UNSUPPORTED;
   if (n_new < 0) return MLA_ERR_BAD_SHAPE;
   if (n_new > 0 && B > 0 && !kv_new) return MLA_ERR_NULL_PTR;
   return decode_impl(q, kv_cache, MLA_CACHE_FP8_E4M3, kv_scale, scale_mode, block_table, seq_lens, B,
                      n_q, H, max_blocks, num_pages, softmax_scale, pages_per_split, max_splits,
-                     o_partial, lse_partial, out, lse, n_new > 0 ? kv_new : nullptr, n_new, stream);
+                     o_partial, lse_partial, out, lse, n_new > 0 ? kv_new : nullptr, n_new, store_rows,
+                     stream);
 }
 
 int mla_decode_combine(const void* o_partial, const float* lse_partial, const int32_t* seq_lens,
                        int B, int n_q, int H, int max_blocks, int pages_per_split, int max_splits,
-                       void* out, float* lse, void* stream) {
+                       void* out, float* lse, const int32_t* status, void* stream) {
   if (bad_stream_free_shape(B, n_q, H)) return MLA_ERR_BAD_SHAPE;
   if (max_blocks < 1 || pages_per_split < 1 || max_splits < 1) return MLA_ERR_BAD_SHAPE;
   if ((int64_t)B * n_q * H * 4 > kMaxGrid) return MLA_ERR_BAD_SHAPE;
@@ -176,6 +179,7 @@ int mla_decode_combine(const void* o_partial, const float* lse_partial, const in
   a.seq_lens = seq_lens;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
+  a.status = status;
   a.B = B;
   a.R = n_q * H;
   a.max_blocks = max_blocks;

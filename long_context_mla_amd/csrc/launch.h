@@ -46,6 +46,7 @@ struct DecodeArgs {
   int n_new;
   uint8_t* cache_out;
   float* scale_out;
+  int store_rows;           // 0: the appended rows serve this launch only, nothing is stored
 };
 
 struct CombineArgs {
@@ -54,6 +55,7 @@ struct CombineArgs {
   const int32_t* seq_lens;
   uint16_t* out;
   float* lse;
+  const int32_t* status;    // [B] or null: requests with a non-zero entry get out = 0, lse = -inf
   int B, R, max_blocks, pps, max_splits;
 };
 

@@ -35,7 +35,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
   const int L = min(max(a.seq_lens[b], 0), a.max_blocks * kPage);
   const int n_pages = (L + kPage - 1) / kPage;
-  const int n_b = min(a.max_splits, (n_pages + a.pps - 1) / a.pps);
+  // a request the page check flagged merges no split: its rows come out 0 / -inf
+  const int n_b = (a.status && a.status[b]) ? 0 : min(a.max_splits, (n_pages + a.pps - 1) / a.pps);
   const float* lse_b = a.lse_part + (int64_t)b * a.max_splits * a.R + r;
   const uint16_t* o_b = a.o_part + ((int64_t)b * a.max_splits * a.R + r) * kDV + chunk * 128 + c4 * 4;
   const int64_t o_stride = (int64_t)a.R * kDV;

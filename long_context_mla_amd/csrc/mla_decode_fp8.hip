@@ -253,7 +253,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     // page it: the wave encodes each one exactly as kv_append_fp8 does and
     // puts it over the row the copy brought (the cache still held the old
     // contents); row group 0 also writes it, and its per-token scale, to the
-    // cache for later steps.  Both row groups compute the same bytes, so it
+    // cache for later steps (unless the caller stores the rows itself).  Both row groups compute the same bytes, so it
     // does not matter which copy the other group's page read saw.
     auto patch_new_rows = [&](int it, uint8_t* kv) {
       const int t_first = (p_begin + it) * kPage + qw * 16;
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
             *reinterpret_cast<u32x2*>(kv + pslot(t, c8 >> 1) * 16 + 8 * (c8 & 1)) = codes[c];
         }
         if (SCALE == kScaleToken && lane == 0) s_scale[it % T::NBUF][t] = sc;
-        if (rg == 0) {
+        if (rg == 0 && a.store_rows) {
           const int pg = min(max(load_const(a.block_table, bt_row + pos / kPage), 0), a.num_pages - 1);
           uint8_t* dst = a.cache_out + ((int64_t)pg * kPage + t) * kD;
           *reinterpret_cast<u32x2*>(dst + 8 * lane) = codes[0];

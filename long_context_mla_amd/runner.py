@@ -16,10 +16,14 @@ from . import _lib
 
 class DecodeStep:
     def __init__(self, B, n_q, H, max_blocks, max_seq_len, total_seq_len, device, num_cus=0,
-                 pages_per_split=None, max_splits=None, fuse_append=True, seq_lens_host=None):
+                 pages_per_split=None, max_splits=None, fuse_append=True, seq_lens_host=None,
+                 overlap_check=False):
         """seq_lens_host: the batch's lengths on the host, when known; the split
         plan is then fitted to them (mla_decode_plan_lens) instead of to the
-        longest and the summed length alone."""
+        longest and the summed length alone.  overlap_check: run the page check
+        beside the decode on a second stream (see _overlapped) instead of in
+        front of it; off by default, since under HIP graphs on this stack the
+        two branches ran one after the other and the step got slower."""
         self.fuse_append = fuse_append
         if pages_per_split is None or max_splits is None:
             if seq_lens_host is not None:
@@ -39,6 +43,7 @@ class DecodeStep:
         else:
             self.o_partial = self.lse_partial = None
         self.status = self.checked_lens = None
+        self.overlap_check = overlap_check
 
     def decode(self, q, kv_cache, kv_scale, scale_mode, block_table, seq_lens, softmax_scale,
                stream=None):
@@ -46,16 +51,20 @@ class DecodeStep:
                               softmax_scale, self.pps, self.max_splits, self.o_partial,
                               self.lse_partial, self.out, self.lse, stream=stream)
 
-    def combine(self, seq_lens, stream=None):
+    def combine(self, seq_lens, stream=None, status=None):
         if self.max_splits > 1:
             _lib.mla_decode_combine(self.o_partial, self.lse_partial, seq_lens, self.max_blocks,
-                                    self.pps, self.out, self.lse, stream=stream)
+                                    self.pps, self.out, self.lse, stream=stream, status=status)
+
+    def _check_buffers(self, device):
+        if self.status is None:
+            self.status = torch.empty(self.B, dtype=torch.int32, device=device)
+            self.checked_lens = torch.empty(self.B, dtype=torch.int32, device=device)
+            self.side = torch.cuda.Stream(device=device)
 
     def check(self, page_tags, block_table, expected_tags, seq_lens, expected_pages=None, stream=None):
         """kv_check_pages into this step's status / checked_lens; returns checked_lens."""
-        if self.status is None:
-            self.status = torch.empty(self.B, dtype=torch.int32, device=block_table.device)
-            self.checked_lens = torch.empty(self.B, dtype=torch.int32, device=block_table.device)
+        self._check_buffers(block_table.device)
         _lib.kv_check_pages(page_tags, block_table, expected_tags, seq_lens, self.status,
                             self.checked_lens, expected_pages, stream=stream)
         return self.checked_lens
@@ -63,9 +72,14 @@ class DecodeStep:
     def __call__(self, q, kv_cache, kv_scale, scale_mode, block_table, seq_lens, softmax_scale,
                  new_rows=None, stream=None, page_check=None):
         """page_check: (page_tags, expected_tags, expected_pages or None) to run the
-        page-tag check first."""
+        page-tag check in this step."""
         if page_check is not None:
             page_tags, expected_tags, expected_pages = page_check
+            fused = new_rows is not None and new_rows.shape[1] > 0 and self.fuse_append
+            if fused and self.max_splits > 1 and self.overlap_check:
+                return self._overlapped(q, kv_cache, kv_scale, scale_mode, block_table, seq_lens,
+                                        softmax_scale, new_rows, stream, page_tags, expected_tags,
+                                        expected_pages)
             seq_lens = self.check(page_tags, block_table, expected_tags, seq_lens, expected_pages, stream)
         if new_rows is not None and new_rows.shape[1] > 0:
             if self.fuse_append:
@@ -79,4 +93,26 @@ class DecodeStep:
                                stream=stream)
         self.decode(q, kv_cache, kv_scale, scale_mode, block_table, seq_lens, softmax_scale, stream)
         self.combine(seq_lens, stream)
+        return self.out, self.lse
+
+    def _overlapped(self, q, kv_cache, kv_scale, scale_mode, block_table, seq_lens, softmax_scale,
+                    new_rows, stream, page_tags, expected_tags, expected_pages):
+        """The page check off the decode's critical path.  A side stream runs
+        kv_check_pages and then kv_append_fp8 on the checked lengths (only
+        requests that passed store their new rows); meanwhile the decode
+        attends with the new rows but stores none, and reads the unchecked
+        lengths (page ids are clamped, so it stays inside the cache).  The
+        combine waits for both and gives flagged requests 0 / -inf rows."""
+        main = stream if stream is not None else torch.cuda.current_stream()
+        self._check_buffers(block_table.device)
+        side = self.side
+        side.wait_stream(main)
+        self.check(page_tags, block_table, expected_tags, seq_lens, expected_pages, stream=side)
+        _lib.kv_append_fp8(new_rows, kv_cache, kv_scale, scale_mode, block_table, self.checked_lens,
+                           stream=side)
+        _lib.mla_decode_paged_append(new_rows, q, kv_cache, kv_scale, scale_mode, block_table, seq_lens,
+                                     softmax_scale, self.pps, self.max_splits, self.o_partial,
+                                     self.lse_partial, self.out, self.lse, stream=main, store_rows=False)
+        main.wait_stream(side)
+        self.combine(seq_lens, main, status=self.status)
         return self.out, self.lse

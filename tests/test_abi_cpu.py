@@ -78,9 +78,9 @@ def test_append_and_combine_validation(lib):
     assert lib.kv_append_fp8(None, P(1), P(1), 2, P(1), P(1), 1, 1, 1, 1, None) == 1
     assert lib.kv_append_fp8(P(1), P(1), P(1), 2, P(1), P(1), -1, 1, 1, 1, None) == 2
     assert lib.kv_append_fp8(None, None, None, 2, None, None, 0, 4, 1, 1, None) == 0
-    assert lib.mla_decode_combine(None, P(1), P(1), 1, 1, 1, 1, 1, 2, P(1), P(1), None) == 1
-    assert lib.mla_decode_combine(P(1), P(1), P(1), 1, 1, 1, 1, 0, 2, P(1), P(1), None) == 2
-    assert lib.mla_decode_combine(P(1), P(1), P(1), 1, 9, 1, 1, 1, 2, P(1), P(1), None) == 2
+    assert lib.mla_decode_combine(None, P(1), P(1), 1, 1, 1, 1, 1, 2, P(1), P(1), None, None) == 1
+    assert lib.mla_decode_combine(P(1), P(1), P(1), 1, 1, 1, 1, 0, 2, P(1), P(1), None, None) == 2
+    assert lib.mla_decode_combine(P(1), P(1), P(1), 1, 9, 1, 1, 1, 2, P(1), P(1), None, None) == 2
     assert lib.mla_status_string(3) == b"unsupported configuration"
 
 

@@ -108,10 +108,7 @@ def test_empty_batch_launches_nothing():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("fuse_append", [True, False])
-def test_flagged_request_is_aborted_within_the_step(fuse_append):
-    import long_context_mla_amd as mla
-
+def _e2e_workload():
     w = synth.custom("check_e2e", B=4, n_q=1, H=64, context_lens=(300, 200, 1000, 65), cache_dtype="fp8",
                      scale_mode="token", seed=5)
     rng = np.random.default_rng(9)
@@ -122,16 +119,36 @@ def test_flagged_request_is_aborted_within_the_step(fuse_append):
     last = (int(w.seq_lens[victim]) - 1) // 64  # the page the victim's new row goes to
     page = int(bt[victim, last])
     tags[page] ^= np.uint32(1)  # the page was handed out again
-    want_s, want_l = oi.check_pages_ref(tags, bt, et, w.seq_lens)
-    log(f"e2e fuse_append={fuse_append} L={w.seq_lens.tolist()} status={want_s.tolist()}")
+    return w, tags, et, victim, page
+
+
+def _e2e_step(w, g, tags, et, fuse_append, overlap, stream=None):
+    import long_context_mla_amd as mla
+
+    npg = int(-(-w.seq_lens.max() // 64))
+    st = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(), g.device,
+                        pages_per_split=2, max_splits=-(-npg // 2), fuse_append=fuse_append,
+                        overlap_check=overlap)
+    check = (_dev(tags), _dev(et), None)
+    return st, check
+
+
+MODES = [("fused", True, False), ("fused_overlapped", True, True), ("separate", False, False)]
+
+
+@pytest.mark.parametrize("mode", MODES, ids=[m[0] for m in MODES])
+def test_flagged_request_is_aborted_within_the_step(mode):
+    name, fuse_append, overlap = mode
+    w, tags, et, victim, page = _e2e_workload()
+    want_s, want_l = oi.check_pages_ref(tags, w.block_table, et, w.seq_lens)
+    log(f"e2e {name} L={w.seq_lens.tolist()} status={want_s.tolist()}")
     assert want_s.tolist() == [0, oi.STALE_TAG, 0, 0]
 
     g = GpuState(w)
     before = g.cache[page].clone()
-    st = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(), g.device,
-                        fuse_append=fuse_append, seq_lens_host=w.seq_lens)
+    st, check = _e2e_step(w, g, tags, et, fuse_append, overlap)
     out, lse = st(g.q, g.cache, g.kv_scale, g.scale_mode, g.block_table, g.seq_lens, w.softmax_scale,
-                  new_rows=g.new_rows, page_check=(_dev(tags), _dev(et), None))
+                  new_rows=g.new_rows, page_check=check)
     torch.cuda.synchronize()
     assert st.status.cpu().numpy().tolist() == want_s.tolist()
     assert st.checked_lens.cpu().numpy().tolist() == want_l.tolist()
@@ -141,4 +158,43 @@ def test_flagged_request_is_aborted_within_the_step(fuse_append):
     assert torch.equal(g.cache[page], before), "an aborted request wrote into the cache"
     keep = [0, 2, 3]
     ref_o, ref_l = oracle_decode(w, requests=keep)
-    compare(o, l, ref_o, ref_l, requests=keep, tag=f"e2e fuse_append={fuse_append}")
+    compare(o, l, ref_o, ref_l, requests=keep, tag=f"e2e {name}")
+
+
+def test_overlapped_check_matches_the_sequential_one():
+    """The check beside the decode (side stream) against the check in front of
+    it: same outputs, same cache bytes and scales after the step, bit for bit;
+    and a HIP graph of the overlapped step gives the same on every replay."""
+    w, tags, et, victim, page = _e2e_workload()
+    res = {}
+    for name, overlap in (("sequential", False), ("overlapped", True)):
+        g = GpuState(w)
+        st, check = _e2e_step(w, g, tags, et, True, overlap)
+        out, lse = st(g.q, g.cache, g.kv_scale, g.scale_mode, g.block_table, g.seq_lens, w.softmax_scale,
+                      new_rows=g.new_rows, page_check=check)
+        torch.cuda.synchronize()
+        res[name] = (out.clone(), lse.clone(), g.cache.clone(), g.kv_scale.clone())
+        if overlap:
+            eager = res[name]
+            graph = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(graph, stream=cap):
+                    st(g.q, g.cache, g.kv_scale, g.scale_mode, g.block_table, g.seq_lens, w.softmax_scale,
+                       new_rows=g.new_rows, page_check=check, stream=cap)
+            torch.cuda.current_stream().wait_stream(cap)
+            for rep in range(3):
+                st.out.zero_()
+                st.lse.zero_()
+                st.status.fill_(-1)
+                torch.cuda.synchronize()
+                graph.replay()
+                torch.cuda.synchronize()
+                log(f"graph replay {rep}")
+                assert torch.equal(st.out, eager[0]) and torch.equal(st.lse, eager[1])
+                assert torch.equal(g.cache, eager[2]) and torch.equal(g.kv_scale, eager[3])
+                assert st.status.cpu().numpy().tolist() == [0, oi.STALE_TAG, 0, 0]
+    a, b = res["sequential"], res["overlapped"]
+    for k, nm in enumerate(("out", "lse", "cache", "kv_scale")):
+        assert torch.equal(a[k], b[k]), nm
