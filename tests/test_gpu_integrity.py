@@ -198,3 +198,31 @@ def test_overlapped_check_matches_the_sequential_one():
     a, b = res["sequential"], res["overlapped"]
     for k, nm in enumerate(("out", "lse", "cache", "kv_scale")):
         assert torch.equal(a[k], b[k]), nm
+
+
+@pytest.mark.parametrize("name", ["fp8_single_100k", "fp8_prefix_shared_b32", "fp8_pool_b64", "bf16_pool_b32",
+                                  "fp8_spec4_b16"])
+def test_full_size_page_maps(name):
+    """The check on the page maps of the named workloads at their full sizes (the
+    shapes the benchmark times), with faults planted at random pages."""
+    w = synth.make(name)
+    rng = np.random.default_rng(2024)
+    bt = w.block_table.copy()
+    tags = rng.integers(0, 2**32, size=w.num_pages, dtype=np.uint64).astype(np.uint32)
+    et = np.where(bt >= 0, tags[np.clip(bt, 0, w.num_pages - 1)], 0).astype(np.uint32)
+    ep = bt.copy()
+    lens = w.seq_lens.copy()
+    npg = (lens.astype(np.int64) + 63) // 64
+    picks = rng.choice(w.B, size=min(w.B, 4), replace=False)
+    for k, b in enumerate(picks):
+        j = int(rng.integers(0, npg[b]))
+        if k == 0:
+            tags[bt[b, j]] ^= np.uint32(1 << 31)  # handed out again (shared pages flag every sharer)
+        elif k == 1:
+            bt[b, j] = (bt[b, j] + 1) % w.num_pages
+        elif k == 2:
+            bt[b, j] = w.num_pages
+        else:
+            lens[b] = w.max_blocks * 64 + 1
+    c = si.TagCase(tags, bt, ep, et, lens)
+    _assert_same(c, f"{name} B={w.B} pages={int(npg.sum())}")
