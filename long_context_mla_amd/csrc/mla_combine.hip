@@ -13,6 +13,7 @@
 namespace mla {
 
 constexpr int kWeightChunk = 1024;  // split weights held in LDS at a time
+constexpr int kHeldSplits = 128;   // splits whose partials a lane holds in registers at once
 
 // Four consecutive bf16 partial values (8 bytes) as floats (exact).
 __device__ __forceinline__ f32x4 load_bf16x4(const uint16_t* p) {
@@ -33,45 +34,79 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   __shared__ f32x4 s_acc[8][32];
   __shared__ float s_ws[8];
 
+  const float* lse_b = a.lse_part + (int64_t)b * a.max_splits * a.R + r;
+  const uint16_t* o_b = a.o_part + ((int64_t)b * a.max_splits * a.R + r) * kDV + chunk * 128 + c4 * 4;
+  const int64_t o_stride = (int64_t)a.R * kDV;
+  // Up to kHeldSplits splits (the usual case) each thread's split LSE is
+  // loaded before the length is known (every entry below max_splits lies in
+  // the buffer; the ones past the request's splits are masked once the length
+  // arrives), and each lane's partials are all loaded at once: two memory
+  // round trips instead of one per pass over the splits.
+  const bool held = a.max_splits <= kHeldSplits;
+  float ls_held = -INFINITY;
+  if (held && t < a.max_splits) ls_held = lse_b[(int64_t)t * a.R];
+
   const int L = min(max(a.seq_lens[b], 0), a.max_blocks * kPage);
   const int n_pages = (L + kPage - 1) / kPage;
   // a request the page check flagged merges no split: its rows come out 0 / -inf
   const int n_b = (a.status && a.status[b]) ? 0 : min(a.max_splits, (n_pages + a.pps - 1) / a.pps);
-  const float* lse_b = a.lse_part + (int64_t)b * a.max_splits * a.R + r;
-  const uint16_t* o_b = a.o_part + ((int64_t)b * a.max_splits * a.R + r) * kDV + chunk * 128 + c4 * 4;
-  const int64_t o_stride = (int64_t)a.R * kDV;
-
-  float M = -INFINITY;
-  for (int s = t; s < n_b; s += 256) M = fmaxf(M, lse_b[(int64_t)s * a.R]);
-  M = wave_max(M);
-  if ((t & 63) == 0) s_red[t >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.0f;
-  for (int s0 = 0; s0 < n_b; s0 += kWeightChunk) {
-    const int s1 = min(n_b, s0 + kWeightChunk);
+  float M = -INFINITY;
+  if (held) {
+    f32x4 o[kHeldSplits / 8];
+    const int last = max(n_b - 1, 0);
+#pragma unroll
+    for (int k = 0; k < kHeldSplits / 8; ++k) o[k] = load_bf16x4(o_b + min(g + 8 * k, last) * o_stride);
+    const float ls = t < n_b ? ls_held : -INFINITY;
+    M = wave_max(ls);
+    if ((t & 63) == 0) s_red[t >> 6] = M;
     __syncthreads();
-    for (int s = s0 + t; s < s1; s += 256) {
-      const float ls = lse_b[(int64_t)s * a.R];
-      s_w[s - s0] = (ls == -INFINITY) ? 0.0f : expf(ls - M);
-    }
+    M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    if (t < kHeldSplits) s_w[t] = (ls == -INFINITY) ? 0.0f : expf(ls - M);
     __syncthreads();
-    int s = s0 + g;
-    for (; s + 24 < s1; s += 32) {
-      const f32x4 o0 = load_bf16x4(o_b + s * o_stride);
-      const f32x4 o1 = load_bf16x4(o_b + (s + 8) * o_stride);
-      const f32x4 o2 = load_bf16x4(o_b + (s + 16) * o_stride);
-      const f32x4 o3 = load_bf16x4(o_b + (s + 24) * o_stride);
-      const float w0 = s_w[s - s0], w1 = s_w[s + 8 - s0], w2 = s_w[s + 16 - s0], w3 = s_w[s + 24 - s0];
-      acc += w0 * o0 + w1 * o1 + w2 * o2 + w3 * o3;
-      wsum += (w0 + w1) + (w2 + w3);
+    // Lanes past n_b hold a copy of split n_b - 1 (finite) and take weight 0.
+    // With n_b == 0 the loads read split 0, which may never have been
+    // written: nothing is accumulated then.
+    if (n_b > 0) {
+#pragma unroll
+      for (int k = 0; k < kHeldSplits / 8; ++k) {
+        const float w = g + 8 * k < n_b ? s_w[g + 8 * k] : 0.0f;
+        acc += w * o[k];
+        wsum += w;
+      }
     }
-    for (; s < s1; s += 8) {
-      const float w = s_w[s - s0];
-      acc += w * load_bf16x4(o_b + s * o_stride);
-      wsum += w;
+  } else {
+    for (int s = t; s < n_b; s += 256) M = fmaxf(M, lse_b[(int64_t)s * a.R]);
+    M = wave_max(M);
+    if ((t & 63) == 0) s_red[t >> 6] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+
+    for (int s0 = 0; s0 < n_b; s0 += kWeightChunk) {
+      const int s1 = min(n_b, s0 + kWeightChunk);
+      __syncthreads();
+      for (int s = s0 + t; s < s1; s += 256) {
+        const float ls = lse_b[(int64_t)s * a.R];
+        s_w[s - s0] = (ls == -INFINITY) ? 0.0f : expf(ls - M);
+      }
+      __syncthreads();
+      int s = s0 + g;
+      for (; s + 24 < s1; s += 32) {
+        const f32x4 o0 = load_bf16x4(o_b + s * o_stride);
+        const f32x4 o1 = load_bf16x4(o_b + (s + 8) * o_stride);
+        const f32x4 o2 = load_bf16x4(o_b + (s + 16) * o_stride);
+        const f32x4 o3 = load_bf16x4(o_b + (s + 24) * o_stride);
+        const float w0 = s_w[s - s0], w1 = s_w[s + 8 - s0], w2 = s_w[s + 16 - s0], w3 = s_w[s + 24 - s0];
+        acc += w0 * o0 + w1 * o1 + w2 * o2 + w3 * o3;
+        wsum += (w0 + w1) + (w2 + w3);
+      }
+      for (; s < s1; s += 8) {
+        const float w = s_w[s - s0];
+        acc += w * load_bf16x4(o_b + s * o_stride);
+        wsum += w;
+      }
     }
   }
   s_acc[g][c4] = acc;
