@@ -21,6 +21,34 @@ __device__ __forceinline__ f32x4 load_bf16x4(const uint16_t* p) {
   return f32x4{float_of(w.x << 16), float_of(w.x & 0xffff0000u), float_of(w.y << 16), float_of(w.y & 0xffff0000u)};
 }
 
+// The merge of one (request, row, chunk) when its n_b splits fit NK loads per
+// lane (8 * NK >= n_b >= 1): lane group g = t / 32 loads splits g + 8k (the
+// ones past n_b repeat split n_b - 1, a finite partial, and take weight 0),
+// all before the block-wide max of the LSEs; then the weights go through LDS
+// and the partials are summed from registers.
+template <int NK>
+__device__ __forceinline__ void merge_held(const uint16_t* o_b, int64_t o_stride, float ls, int n_b,
+                                           float* s_w, float* s_red, f32x4& acc, float& wsum,
+                                           float& M) {
+  const int t = threadIdx.x;
+  const int g = t >> 5;
+  f32x4 o[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) o[k] = load_bf16x4(o_b + min(g + 8 * k, n_b - 1) * o_stride);
+  M = wave_max(ls);
+  if ((t & 63) == 0) s_red[t >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  if (t < 8 * NK) s_w[t] = (ls == -INFINITY) ? 0.0f : expf(ls - M);
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const float w = g + 8 * k < n_b ? s_w[g + 8 * k] : 0.0f;
+    acc += w * o[k];
+    wsum += w;
+  }
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int chunk = blockIdx.x & 3;
   const int br = blockIdx.x >> 2;  // b * R + r
@@ -40,8 +68,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   // Up to kHeldSplits splits (the usual case) each thread's split LSE is
   // loaded before the length is known (every entry below max_splits lies in
   // the buffer; the ones past the request's splits are masked once the length
-  // arrives), and each lane's partials are all loaded at once: two memory
-  // round trips instead of one per pass over the splits.
+  // arrives), and each lane's partials for the request's splits are all
+  // loaded at once: two memory round trips instead of one per pass over the
+  // splits.
   const bool held = a.max_splits <= kHeldSplits;
   float ls_held = -INFINITY;
   if (held && t < a.max_splits) ls_held = lse_b[(int64_t)t * a.R];
@@ -55,28 +84,22 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   float wsum = 0.0f;
   float M = -INFINITY;
   if (held) {
-    f32x4 o[kHeldSplits / 8];
-    const int last = max(n_b - 1, 0);
-#pragma unroll
-    for (int k = 0; k < kHeldSplits / 8; ++k) o[k] = load_bf16x4(o_b + min(g + 8 * k, last) * o_stride);
+    // Each group of 32 lanes takes splits g, g + 8, ...: ceil(n_b / 8) loads
+    // per lane, rounded up to a power of two so that each count is straight-line
+    // code with every load in flight at once (the count is uniform over the
+    // workgroup).  An empty request (n_b == 0) merges nothing.
     const float ls = t < n_b ? ls_held : -INFINITY;
-    M = wave_max(ls);
-    if ((t & 63) == 0) s_red[t >> 6] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    if (t < kHeldSplits) s_w[t] = (ls == -INFINITY) ? 0.0f : expf(ls - M);
-    __syncthreads();
-    // Lanes past n_b hold a copy of split n_b - 1 (finite) and take weight 0.
-    // With n_b == 0 the loads read split 0, which may never have been
-    // written: nothing is accumulated then.
-    if (n_b > 0) {
-#pragma unroll
-      for (int k = 0; k < kHeldSplits / 8; ++k) {
-        const float w = g + 8 * k < n_b ? s_w[g + 8 * k] : 0.0f;
-        acc += w * o[k];
-        wsum += w;
-      }
-    }
+    const int n_k = (n_b + 7) >> 3;
+    if (n_k > 8)
+      merge_held<16>(o_b, o_stride, ls, n_b, s_w, s_red, acc, wsum, M);
+    else if (n_k > 4)
+      merge_held<8>(o_b, o_stride, ls, n_b, s_w, s_red, acc, wsum, M);
+    else if (n_k > 2)
+      merge_held<4>(o_b, o_stride, ls, n_b, s_w, s_red, acc, wsum, M);
+    else if (n_k > 1)
+      merge_held<2>(o_b, o_stride, ls, n_b, s_w, s_red, acc, wsum, M);
+    else if (n_k == 1)
+      merge_held<1>(o_b, o_stride, ls, n_b, s_w, s_red, acc, wsum, M);
   } else {
     for (int s = t; s < n_b; s += 256) M = fmaxf(M, lse_b[(int64_t)s * a.R]);
     M = wave_max(M);
