@@ -148,11 +148,11 @@ def cpu_baseline(w, repeats, seconds):
 
 
 def time_page_check(args, w, mla, torch, np, dev, stream, cap, step, bt, sl, run_checked, graphs):
-    """The KV page-tag check (kv_check_pages): its kernel alone (back to back
-    inside one HIP graph), and the step's HIP graph without it, with it in front
-    of the decode, and with it beside the decode on a second stream (the append
-    on the checked lengths after it, the combine masking flagged requests),
-    replayed in alternating rounds (the median round of each)."""
+    """The KV page-tag check: kv_check_pages alone (back to back inside one HIP
+    graph), and the step's HIP graph without the check, with it inside the
+    decode launch (mla_decode_paged_append_checked, the default: overhead_frac),
+    in front of the decode, and beside the decode on a second stream, replayed
+    in alternating rounds (the median round of each)."""
     rng = np.random.default_rng(77)
     tags = rng.integers(0, 2**32, size=w.num_pages, dtype=np.uint64).astype(np.uint32)
     bt_h = w.block_table
@@ -181,8 +181,8 @@ def time_page_check(args, w, mla, torch, np, dev, stream, cap, step, bt, sl, run
     torch.cuda.synchronize()
     k_us = start.elapsed_time(end) / (reps * 20) * 1000
     graphs_by_mode = {"plain": graphs}
-    for mode, overlap in (("sequential", False), ("overlapped", True)):
-        step.overlap_check = overlap
+    for mode, cm in (("sequential", "front"), ("overlapped", "stream"), ("in_launch", "launch")):
+        step.check_mode = cm
         gs = []
         cap.wait_stream(stream)
         with torch.cuda.stream(cap):
@@ -193,7 +193,7 @@ def time_page_check(args, w, mla, torch, np, dev, stream, cap, step, bt, sl, run
                 gs.append(g)
         stream.wait_stream(cap)
         graphs_by_mode[mode] = gs
-    step.overlap_check = False
+    step.check_mode = "launch"
     for gs in graphs_by_mode.values():
         for i in range(args.warmup):
             gs[i % args.rotate].replay()
@@ -218,7 +218,9 @@ def time_page_check(args, w, mla, torch, np, dev, stream, cap, step, bt, sl, run
         "ms_per_step_graph_plain": round(med["plain"], 5),
         "ms_per_step_graph_check_first": round(med["sequential"], 5),
         "ms_per_step_graph_check_beside": round(med["overlapped"], 5),
-        "overhead_frac": round(med["sequential"] / med["plain"] - 1.0, 4),
+        "ms_per_step_graph_check_in_launch": round(med["in_launch"], 5),
+        "overhead_frac": round(med["in_launch"] / med["plain"] - 1.0, 4),
+        "overhead_frac_check_first": round(med["sequential"] / med["plain"] - 1.0, 4),
         "overhead_frac_check_beside": round(med["overlapped"] / med["plain"] - 1.0, 4),
         "flagged_requests": flagged,
     }

@@ -177,6 +177,37 @@ int mla_decode_paged_append(const void* kv_new, int n_new, const void* q, void* 
                             void* stream);
 
 /*
+ * mla_decode_paged_append_checked — mla_decode_paged_append (rows stored,
+ * split partials written) with the KV page-tag check of kv_check_pages
+ * carried in the same launch ("Smaller, faster, safer", section "Protecting a
+ * shared KV cache").  B extra workgroups, placed after the decode's, each
+ * check one request and write status[b] exactly as kv_check_pages does.  The
+ * attention does not wait for them: it reads the unchecked lengths (page ids
+ * are clamped, so it stays inside the cache), and the flagged requests are
+ * masked afterwards by mla_decode_combine with the same status array, so no
+ * flagged request returns data.  Each new row is stored only into a page
+ * that passes the check on its own (in the pool, equal to the recorded page,
+ * carrying the recorded tag), so nothing is written into a page that was
+ * handed to another request.  (A flagged request can still store its rows
+ * into its own pages that pass; kv_check_pages in front of the decode stores
+ * none of a flagged request's rows.)
+ *   page_tags, expected_pages (or NULL), expected_tags, status: as in
+ *               kv_check_pages.
+ *   the rest    as in mla_decode_paged_append with max_splits >= 2 (out and
+ *               lse come from mla_decode_combine, which must get `status`).
+ * Returns MLA_ERR_UNSUPPORTED for max_splits < 2 or MLA_SCALE_NONE,
+ * MLA_ERR_NULL_PTR for a NULL check array with B > 0; otherwise as
+ * mla_decode_paged_append.
+ */
+int mla_decode_paged_append_checked(const void* kv_new, int n_new, const void* q, void* kv_cache,
+                                    float* kv_scale, int scale_mode, const int32_t* block_table,
+                                    const int32_t* seq_lens, int B, int n_q, int H, int max_blocks,
+                                    int num_pages, float softmax_scale, int pages_per_split,
+                                    int max_splits, void* o_partial, float* lse_partial,
+                                    const uint32_t* page_tags, const int32_t* expected_pages,
+                                    const uint32_t* expected_tags, int32_t* status, void* stream);
+
+/*
  * mla_decode_combine — merge the split partials of mla_decode_paged
  * ("vLLM x AgentX", section "Model-specific parallelism / Kimi K3": partial
  * outputs and LSE statistics merged with online softmax).

@@ -54,17 +54,19 @@ def _load() -> ctypes.CDLL:
     lib.mla_decode_plan.argtypes = [I, I, I, I, L, I, ctypes.POINTER(I), ctypes.POINTER(I)]
     lib.mla_decode_plan_lens.argtypes = [P, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
     lib.kv_check_pages.argtypes = [P, I, P, P, P, P, I, I, P, P, P]
+    lib.mla_decode_paged_append_checked.argtypes = [P, I, P, P, P, I, P, P, I, I, I, I, I, F, I, I, P, P,
+                                                    P, P, P, P, P]
     lib.mla_status_string.argtypes = [I]
     lib.mla_status_string.restype = ctypes.c_char_p
     for fn in ("kv_append_fp8", "mla_decode_paged", "mla_decode_paged_append", "mla_decode_combine",
-               "mla_decode_plan", "mla_decode_plan_lens", "kv_check_pages"):
+               "mla_decode_plan", "mla_decode_plan_lens", "kv_check_pages", "mla_decode_paged_append_checked"):
         getattr(lib, fn).restype = I
     return lib
 
 
 LIB = _load()
-EXPORTS = ("kv_append_fp8", "mla_decode_paged", "mla_decode_paged_append", "mla_decode_combine",
-           "mla_decode_plan", "mla_decode_plan_lens", "kv_check_pages", "mla_status_string")
+EXPORTS = ("kv_append_fp8", "mla_decode_paged", "mla_decode_paged_append", "mla_decode_paged_append_checked",
+           "mla_decode_combine", "mla_decode_plan", "mla_decode_plan_lens", "kv_check_pages", "mla_status_string")
 
 PAGE_OK = 0
 PAGE_BAD_LEN = 1
@@ -309,3 +311,54 @@ def kv_check_pages(page_tags, block_table, expected_tags, seq_lens, status, chec
         _ptr(page_tags), page_tags.shape[0], _ptr(block_table), _ptr(expected_pages),
         _ptr(expected_tags), _ptr(seq_lens), B, max_blocks, _ptr(status), _ptr(checked_lens),
         _stream(stream)))
+
+
+def mla_decode_paged_append_checked(kv_new, q, kv_cache, kv_scale, scale_mode, block_table, seq_lens,
+                                    softmax_scale, pages_per_split, max_splits, o_partial, lse_partial,
+                                    page_tags, expected_tags, status, expected_pages=None, stream=None):
+    """mla_decode_paged_append (max_splits >= 2) with the page-tag check in the same launch:
+    writes status int32 [B]; pass it to mla_decode_combine."""
+    mode = _SCALE_NAMES[scale_mode] if isinstance(scale_mode, str) else int(scale_mode)
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 4)
+    _need(kv_new, "kv_new", torch.bfloat16, dev, 3)
+    if _cache_kind(kv_cache) != CACHE_FP8_E4M3 or kv_cache.dim() != 3:
+        raise TypeError("kv_cache must be E4M3 codes [num_pages, 64, 576]")
+    _need(kv_cache, "kv_cache", kv_cache.dtype, dev)
+    _need(kv_scale, "kv_scale", torch.float32, dev)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    _need_tags(page_tags, "page_tags", dev, 1)
+    _need_tags(expected_tags, "expected_tags", dev, 2)
+    _need(status, "status", torch.int32, dev, 1)
+    B, n_q, H, D = q.shape
+    num_pages = kv_cache.shape[0]
+    max_blocks = block_table.shape[1]
+    if D != HEAD_DIM or tuple(kv_cache.shape[1:]) != (PAGE_SIZE, HEAD_DIM):
+        raise ValueError("row width must be 576 and pages [64, 576]")
+    if kv_new.shape[0] != B or kv_new.shape[2] != HEAD_DIM:
+        raise ValueError("kv_new must be [B, n_new, 576]")
+    if block_table.shape[0] != B or seq_lens.shape[0] != B or status.shape[0] != B:
+        raise ValueError("block_table / seq_lens / status batch mismatch")
+    if page_tags.shape[0] != num_pages:
+        raise ValueError("page_tags must have num_pages entries")
+    if tuple(expected_tags.shape) != (B, max_blocks):
+        raise ValueError("expected_tags must match block_table's shape")
+    if expected_pages is not None:
+        _need(expected_pages, "expected_pages", torch.int32, dev, 2)
+        if tuple(expected_pages.shape) != (B, max_blocks):
+            raise ValueError("expected_pages must match block_table's shape")
+    if mode == SCALE_PER_TOKEN and tuple(kv_scale.shape) != (num_pages, PAGE_SIZE):
+        raise ValueError("per-token kv_scale must be [num_pages, 64]")
+    if mode == SCALE_PER_TENSOR and kv_scale.numel() != 1:
+        raise ValueError("per-tensor kv_scale must have one element")
+    _need(o_partial, "o_partial", torch.bfloat16, dev)
+    _need(lse_partial, "lse_partial", torch.float32, dev)
+    if tuple(o_partial.shape) != (B, max_splits, n_q, H, VALUE_DIM) or \
+            tuple(lse_partial.shape) != (B, max_splits, n_q, H):
+        raise ValueError("o_partial / lse_partial shape mismatch")
+    _check("mla_decode_paged_append_checked", LIB.mla_decode_paged_append_checked(
+        _ptr(kv_new), kv_new.shape[1], _ptr(q), _ptr(kv_cache), _ptr(kv_scale), mode,
+        _ptr(block_table), _ptr(seq_lens), B, n_q, H, max_blocks, num_pages,
+        float(softmax_scale), int(pages_per_split), int(max_splits), _ptr(o_partial), _ptr(lse_partial),
+        _ptr(page_tags), _ptr(expected_pages), _ptr(expected_tags), _ptr(status), _stream(stream)))

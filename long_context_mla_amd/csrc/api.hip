@@ -33,7 +33,9 @@ int decode_impl(const void* q, const void* kv_cache, int cache_dtype, const floa
                 int scale_mode, const int32_t* block_table, const int32_t* seq_lens, int B, int n_q,
                 int H, int max_blocks, int num_pages, float softmax_scale, int pages_per_split,
                 int max_splits, void* o_partial, float* lse_partial, void* out, float* lse,
-                const void* kv_new, int n_new, int store_rows, void* stream) {
+                const void* kv_new, int n_new, int store_rows, void* stream,
+                const uint32_t* page_tags = nullptr, const int32_t* expected_pages = nullptr,
+                const uint32_t* expected_tags = nullptr, int32_t* status = nullptr) {
   if (int s = check_cache_mode(cache_dtype, scale_mode)) return s;
   if (bad_stream_free_shape(B, n_q, H)) return MLA_ERR_BAD_SHAPE;
   if (max_blocks < 1 || num_pages < 1 || pages_per_split < 1 || max_splits < 1) return MLA_ERR_BAD_SHAPE;
@@ -42,7 +44,7 @@ int decode_impl(const void* q, const void* kv_cache, int cache_dtype, const floa
   const int R = n_q * H;
   const int rows = mla::decode_rows_per_group(B, R);
   const int n_rg = (R + rows - 1) / rows;
-  if (mla::decode_grid_size(B, max_splits, n_rg) > kMaxGrid) return MLA_ERR_BAD_SHAPE;
+  if (mla::decode_grid_size(B, max_splits, n_rg) + (status ? B : 0) > kMaxGrid) return MLA_ERR_BAD_SHAPE;
   if (B == 0) return MLA_OK;
   if (!q || !kv_cache || !block_table || !seq_lens) return MLA_ERR_NULL_PTR;
   if (scale_mode != MLA_SCALE_NONE && !kv_scale) return MLA_ERR_NULL_PTR;
@@ -73,6 +75,11 @@ int decode_impl(const void* q, const void* kv_cache, int cache_dtype, const floa
   a.cache_out = static_cast<uint8_t*>(const_cast<void*>(kv_cache));
   a.scale_out = const_cast<float*>(kv_scale);
   a.store_rows = store_rows ? 1 : 0;
+  a.page_tags = page_tags;
+  a.expected_pages = expected_pages ? expected_pages : block_table;  // no record: the map is the record
+  a.expected_tags = expected_tags;
+  a.status = status;
+  a.check_from = (int)mla::decode_grid_size(B, max_splits, n_rg);
   const int kind = cache_dtype == MLA_CACHE_FP8_E4M3 ? mla::kFp8 : mla::kBf16;
   const hipError_t e = mla::launch_decode(a, kind, scale_mode, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
@@ -163,6 +170,23 @@ int mla_decode_paged_append(const void* kv_new, int n_new, const void* q, void* 
                      n_q, H, max_blocks, num_pages, softmax_scale, pages_per_split, max_splits,
                      o_partial, lse_partial, out, lse, n_new > 0 ? kv_new : nullptr, n_new, store_rows,
                      stream);
+}
+
+int mla_decode_paged_append_checked(const void* kv_new, int n_new, const void* q, void* kv_cache,
+                                    float* kv_scale, int scale_mode, const int32_t* block_table,
+                                    const int32_t* seq_lens, int B, int n_q, int H, int max_blocks,
+                                    int num_pages, float softmax_scale, int pages_per_split,
+                                    int max_splits, void* o_partial, float* lse_partial,
+                                    const uint32_t* page_tags, const int32_t* expected_pages,
+                                    const uint32_t* expected_tags, int32_t* status, void* stream) {
+  if (scale_mode != MLA_SCALE_PER_TENSOR && scale_mode != MLA_SCALE_PER_TOKEN) return MLA_ERR_UNSUPPORTED;
+  if (max_splits < 2) return MLA_ERR_UNSUPPORTED;  // the flagged rows are masked by the combine
+  if (n_new < 0) return MLA_ERR_BAD_SHAPE;
+  if (B > 0 && ((n_new > 0 && !kv_new) || !page_tags || !expected_tags || !status)) return MLA_ERR_NULL_PTR;
+  return decode_impl(q, kv_cache, MLA_CACHE_FP8_E4M3, kv_scale, scale_mode, block_table, seq_lens, B,
+                     n_q, H, max_blocks, num_pages, softmax_scale, pages_per_split, max_splits,
+                     o_partial, lse_partial, nullptr, nullptr, n_new > 0 ? kv_new : nullptr, n_new, 1,
+                     stream, page_tags, expected_pages, expected_tags, status);
 }
 
 int mla_decode_combine(const void* o_partial, const float* lse_partial, const int32_t* seq_lens,

@@ -47,6 +47,14 @@ struct DecodeArgs {
   uint8_t* cache_out;
   float* scale_out;
   int store_rows;           // 0: the appended rows serve this launch only, nothing is stored
+  // The page-tag check carried in the same launch (status != null, FP8 only):
+  // workgroups from check_from on each check request blockIdx.x - check_from
+  // and write its status; the rows above are stored only into pages that pass.
+  const uint32_t* page_tags;
+  const int32_t* expected_pages;
+  const uint32_t* expected_tags;
+  int32_t* status;
+  int check_from;
 };
 
 struct CombineArgs {

@@ -33,12 +33,14 @@
 #include <type_traits>
 
 #include "decode_tile.h"
+#include "page_check.h"
 #include "device_common.h"
 #include "launch.h"
 
 namespace mla {
 
-template <int SCALE>
+// CHECKED: the launch also carries the page-tag check (a.status != null).
+template <int SCALE, bool CHECKED>
 __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   using T = Tile<kFp8>;
   // LDS layout of a staged page (36 16-byte chunks per token): token t's
@@ -64,6 +66,28 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   __shared__ float s_lnrm[4][kRows];
   __shared__ float s_m0[kRows];
   __shared__ __attribute__((aligned(16))) uint8_t s_flag[2][4];  // [page parity][score wave]
+
+  // Workgroups past the decode's carry the page-tag check, one per request.
+  // The attention above does not wait for them: flagged requests are masked
+  // by mla_decode_combine (a later launch), and each row store below checks
+  // the page it writes on its own.
+  if (CHECKED && (int)blockIdx.x >= a.check_from) {
+    CheckArgs c;
+    c.page_tags = a.page_tags;
+    c.block_table = a.block_table;
+    c.expected_pages = a.expected_pages;
+    c.expected_tags = a.expected_tags;
+    c.seq_lens = a.seq_lens;
+    c.status = a.status;
+    c.checked_lens = nullptr;
+    c.B = a.B;
+    c.max_blocks = a.max_blocks;
+    c.num_pages = a.num_pages;
+    const int cb = (int)blockIdx.x - a.check_from;
+    const int st = check_request<512>(c, cb, a.seq_lens[cb], reinterpret_cast<int*>(&s_red[0][0]));
+    if (threadIdx.x == 0) a.status[cb] = st;
+    return;
+  }
 
   // One round trip for the launch arguments the first loads need: without
   // this the compiler fetches them in dependent batches.
@@ -271,7 +295,16 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
             *reinterpret_cast<u32x2*>(kv + pslot(t, c8 >> 1) * 16 + 8 * (c8 & 1)) = codes[c];
         }
         if (SCALE == kScaleToken && lane == 0) s_scale[it % T::NBUF][t] = sc;
-        if (rg == 0 && a.store_rows) {
+        bool store = rg == 0 && a.store_rows;
+        if (CHECKED && store) {
+          // the page check runs beside this launch: store only into a page
+          // that is in the pool, is the recorded one and carries its tag
+          const int64_t e = bt_row + pos / kPage;
+          const int raw = load_const(a.block_table, e);
+          store = raw >= 0 && raw < a.num_pages && raw == load_const(a.expected_pages, e) &&
+                  load_const(a.page_tags, raw) == load_const(a.expected_tags, e);
+        }
+        if (store) {
           const int pg = min(max(load_const(a.block_table, bt_row + pos / kPage), 0), a.num_pages - 1);
           uint8_t* dst = a.cache_out + ((int64_t)pg * kPage + t) * kD;
           *reinterpret_cast<u32x2*>(dst + 8 * lane) = codes[0];
@@ -640,16 +673,23 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
 }
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, int scale_mode, hipStream_t stream) {
-  const dim3 grid((unsigned)decode_grid_size(a.B, a.max_splits, a.n_rg)), block(512);
+  const bool checked = a.status != nullptr;
+  const dim3 grid((unsigned)(decode_grid_size(a.B, a.max_splits, a.n_rg) + (checked ? a.B : 0))), block(512);
   switch (scale_mode) {
     case kScaleTensor:
-      hipLaunchKernelGGL((decode_fp8_kernel<kScaleTensor>), grid, block, 0, stream, a);
+      if (checked)
+        hipLaunchKernelGGL((decode_fp8_kernel<kScaleTensor, true>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((decode_fp8_kernel<kScaleTensor, false>), grid, block, 0, stream, a);
       break;
     case kScaleToken:
-      hipLaunchKernelGGL((decode_fp8_kernel<kScaleToken>), grid, block, 0, stream, a);
+      if (checked)
+        hipLaunchKernelGGL((decode_fp8_kernel<kScaleToken, true>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((decode_fp8_kernel<kScaleToken, false>), grid, block, 0, stream, a);
       break;
     default:
-      hipLaunchKernelGGL((decode_fp8_kernel<kScaleNone>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((decode_fp8_kernel<kScaleNone, false>), grid, block, 0, stream, a);
       break;
   }
   return hipGetLastError();

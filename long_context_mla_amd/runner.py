@@ -17,13 +17,16 @@ from . import _lib
 class DecodeStep:
     def __init__(self, B, n_q, H, max_blocks, max_seq_len, total_seq_len, device, num_cus=0,
                  pages_per_split=None, max_splits=None, fuse_append=True, seq_lens_host=None,
-                 overlap_check=False):
+                 check_mode="launch"):
         """seq_lens_host: the batch's lengths on the host, when known; the split
         plan is then fitted to them (mla_decode_plan_lens) instead of to the
-        longest and the summed length alone.  overlap_check: run the page check
-        beside the decode on a second stream (see _overlapped) instead of in
-        front of it; off by default, since under HIP graphs on this stack the
-        two branches ran one after the other and the step got slower."""
+        longest and the summed length alone.  check_mode, where the page check
+        runs when a step gets ``page_check`` (and has new rows on an FP8 cache
+        with more than one split; otherwise it runs in front):
+          "launch"  inside the decode launch (mla_decode_paged_append_checked),
+                    the combine masking flagged requests (the default);
+          "front"   kv_check_pages, then the step on the checked lengths;
+          "stream"  beside the decode on a second stream (see _overlapped)."""
         self.fuse_append = fuse_append
         if pages_per_split is None or max_splits is None:
             if seq_lens_host is not None:
@@ -43,7 +46,9 @@ class DecodeStep:
         else:
             self.o_partial = self.lse_partial = None
         self.status = self.checked_lens = None
-        self.overlap_check = overlap_check
+        if check_mode not in ("front", "launch", "stream"):
+            raise ValueError(f"check_mode must be front, launch or stream, got {check_mode!r}")
+        self.check_mode = check_mode
 
     def decode(self, q, kv_cache, kv_scale, scale_mode, block_table, seq_lens, softmax_scale,
                stream=None):
@@ -76,10 +81,18 @@ class DecodeStep:
         if page_check is not None:
             page_tags, expected_tags, expected_pages = page_check
             fused = new_rows is not None and new_rows.shape[1] > 0 and self.fuse_append
-            if fused and self.max_splits > 1 and self.overlap_check:
+            if fused and self.max_splits > 1 and self.check_mode == "stream":
                 return self._overlapped(q, kv_cache, kv_scale, scale_mode, block_table, seq_lens,
                                         softmax_scale, new_rows, stream, page_tags, expected_tags,
                                         expected_pages)
+            if fused and self.max_splits > 1 and self.check_mode == "launch":
+                self._check_buffers(block_table.device)
+                _lib.mla_decode_paged_append_checked(
+                    new_rows, q, kv_cache, kv_scale, scale_mode, block_table, seq_lens, softmax_scale,
+                    self.pps, self.max_splits, self.o_partial, self.lse_partial, page_tags, expected_tags,
+                    self.status, expected_pages, stream=stream)
+                self.combine(seq_lens, stream, status=self.status)
+                return self.out, self.lse
             seq_lens = self.check(page_tags, block_table, expected_tags, seq_lens, expected_pages, stream)
         if new_rows is not None and new_rows.shape[1] > 0:
             if self.fuse_append:

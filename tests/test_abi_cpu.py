@@ -105,6 +105,22 @@ def test_page_check_validation(lib):
     assert call(B=0, tags=None, bt=None, et=None, sl=None, st=None, cl=None) == 0
 
 
+def test_checked_decode_validation(lib):
+    P = ctypes.c_void_p
+
+    def call(ms=4, tags=1, et=1, st=1, sm=2, B=1):
+        Q = lambda v: None if v is None else P(v)  # noqa: E731
+        return lib.mla_decode_paged_append_checked(P(1), 1, P(1), P(1), P(1), sm, P(1), P(1), B, 1, 64, 10, 10,
+                                                   0.07, 1, ms, P(1), P(1), Q(tags), None, Q(et), Q(st), None)
+
+    assert call(ms=1) == 3  # the flagged rows are masked by the combine: splits required
+    assert call(sm=0) == 3
+    assert call(tags=None) == 1
+    assert call(et=None) == 1
+    assert call(st=None) == 1
+    assert call(B=0, tags=None, et=None, st=None) == 0
+
+
 @pytest.mark.parametrize("B,n_q,H,maxL,total,cus", [
     (1, 1, 64, 100_001, 100_001, 256),
     (32, 1, 64, 137_661, 3_269_170, 256),

@@ -122,23 +122,24 @@ def _e2e_workload():
     return w, tags, et, victim, page
 
 
-def _e2e_step(w, g, tags, et, fuse_append, overlap, stream=None):
+def _e2e_step(w, g, tags, et, fuse_append, check_mode, stream=None):
     import long_context_mla_amd as mla
 
     npg = int(-(-w.seq_lens.max() // 64))
     st = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(), g.device,
                         pages_per_split=2, max_splits=-(-npg // 2), fuse_append=fuse_append,
-                        overlap_check=overlap)
+                        check_mode=check_mode)
     check = (_dev(tags), _dev(et), None)
     return st, check
 
 
-MODES = [("fused", True, False), ("fused_overlapped", True, True), ("separate", False, False)]
+MODES = [("fused", True, "front"), ("fused_overlapped", True, "stream"), ("fused_in_launch", True, "launch"),
+         ("separate", False, "front")]
 
 
 @pytest.mark.parametrize("mode", MODES, ids=[m[0] for m in MODES])
 def test_flagged_request_is_aborted_within_the_step(mode):
-    name, fuse_append, overlap = mode
+    name, fuse_append, check_mode = mode
     w, tags, et, victim, page = _e2e_workload()
     want_s, want_l = oi.check_pages_ref(tags, w.block_table, et, w.seq_lens)
     log(f"e2e {name} L={w.seq_lens.tolist()} status={want_s.tolist()}")
@@ -146,12 +147,13 @@ def test_flagged_request_is_aborted_within_the_step(mode):
 
     g = GpuState(w)
     before = g.cache[page].clone()
-    st, check = _e2e_step(w, g, tags, et, fuse_append, overlap)
+    st, check = _e2e_step(w, g, tags, et, fuse_append, check_mode)
     out, lse = st(g.q, g.cache, g.kv_scale, g.scale_mode, g.block_table, g.seq_lens, w.softmax_scale,
                   new_rows=g.new_rows, page_check=check)
     torch.cuda.synchronize()
     assert st.status.cpu().numpy().tolist() == want_s.tolist()
-    assert st.checked_lens.cpu().numpy().tolist() == want_l.tolist()
+    if check_mode != "launch":  # the in-launch check writes the status only
+        assert st.checked_lens.cpu().numpy().tolist() == want_l.tolist()
     o = bf16_tensor_to_f64(out)
     l = lse.detach().cpu().double().numpy()
     assert not o[victim].any() and np.all(np.isneginf(l[victim]))
@@ -162,19 +164,21 @@ def test_flagged_request_is_aborted_within_the_step(mode):
 
 
 def test_overlapped_check_matches_the_sequential_one():
-    """The check beside the decode (side stream) against the check in front of
-    it: same outputs, same cache bytes and scales after the step, bit for bit;
-    and a HIP graph of the overlapped step gives the same on every replay."""
+    """The check beside the decode (side stream) and inside the decode launch
+    against the check in front of it: same outputs, same cache bytes and scales
+    after the step, bit for bit (the flagged request's stale page is the one
+    its new row goes to, so no mode stores it); and a HIP graph of each step
+    gives the same on every replay."""
     w, tags, et, victim, page = _e2e_workload()
     res = {}
-    for name, overlap in (("sequential", False), ("overlapped", True)):
+    for name, mode in (("sequential", "front"), ("overlapped", "stream"), ("in_launch", "launch")):
         g = GpuState(w)
-        st, check = _e2e_step(w, g, tags, et, True, overlap)
+        st, check = _e2e_step(w, g, tags, et, True, mode)
         out, lse = st(g.q, g.cache, g.kv_scale, g.scale_mode, g.block_table, g.seq_lens, w.softmax_scale,
                       new_rows=g.new_rows, page_check=check)
         torch.cuda.synchronize()
         res[name] = (out.clone(), lse.clone(), g.cache.clone(), g.kv_scale.clone())
-        if overlap:
+        if mode != "front":
             eager = res[name]
             graph = torch.cuda.CUDAGraph()
             cap = torch.cuda.Stream()
@@ -195,9 +199,11 @@ def test_overlapped_check_matches_the_sequential_one():
                 assert torch.equal(st.out, eager[0]) and torch.equal(st.lse, eager[1])
                 assert torch.equal(g.cache, eager[2]) and torch.equal(g.kv_scale, eager[3])
                 assert st.status.cpu().numpy().tolist() == [0, oi.STALE_TAG, 0, 0]
-    a, b = res["sequential"], res["overlapped"]
-    for k, nm in enumerate(("out", "lse", "cache", "kv_scale")):
-        assert torch.equal(a[k], b[k]), nm
+    a = res["sequential"]
+    for other in ("overlapped", "in_launch"):
+        b = res[other]
+        for k, nm in enumerate(("out", "lse", "cache", "kv_scale")):
+            assert torch.equal(a[k], b[k]), (other, nm)
 
 
 @pytest.mark.parametrize("name", ["fp8_single_100k", "fp8_prefix_shared_b32", "fp8_pool_b64", "bf16_pool_b32",
@@ -226,3 +232,40 @@ def test_full_size_page_maps(name):
             lens[b] = w.max_blocks * 64 + 1
     c = si.TagCase(tags, bt, ep, et, lens)
     _assert_same(c, f"{name} B={w.B} pages={int(npg.sum())}")
+
+
+def test_in_launch_check_with_an_earlier_stale_page():
+    """The check inside the decode launch when a flagged request's stale page is
+    not the one its new row goes to: the row is stored into its own last page
+    (which passes), the stale page is left alone, and the request's rows still
+    come out 0 / -inf while the others match the oracle."""
+    import long_context_mla_amd as mla
+
+    w, tags, et, victim, last_page = _e2e_workload()
+    tags[last_page] ^= np.uint32(1)  # undo: the last page passes again
+    first_page = int(w.block_table[victim, 0])
+    tags[first_page] ^= np.uint32(1 << 7)  # the first page was handed out again
+    want_s, _ = oi.check_pages_ref(tags, w.block_table, et, w.seq_lens)
+    assert want_s.tolist() == [0, oi.STALE_TAG, 0, 0]
+    g = GpuState(w)
+    before = g.cache[first_page].clone()
+    st, check = _e2e_step(w, g, tags, et, True, "launch")
+    out, lse = st(g.q, g.cache, g.kv_scale, g.scale_mode, g.block_table, g.seq_lens, w.softmax_scale,
+                  new_rows=g.new_rows, page_check=check)
+    torch.cuda.synchronize()
+    assert st.status.cpu().numpy().tolist() == want_s.tolist()
+    o = bf16_tensor_to_f64(out)
+    l = lse.detach().cpu().double().numpy()
+    assert not o[victim].any() and np.all(np.isneginf(l[victim]))
+    assert torch.equal(g.cache[first_page], before)
+    # the victim's new row went to its own last page, as a check-free append puts it
+    ref = GpuState(w)
+    ref_st = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(), ref.device,
+                            pages_per_split=st.pps, max_splits=st.max_splits)
+    ref_st(ref.q, ref.cache, ref.kv_scale, ref.scale_mode, ref.block_table, ref.seq_lens, w.softmax_scale,
+           new_rows=ref.new_rows)
+    torch.cuda.synchronize()
+    assert torch.equal(g.cache, ref.cache) and torch.equal(g.kv_scale, ref.kv_scale)
+    keep = [0, 2, 3]
+    ref_o, ref_l = oracle_decode(w, requests=keep)
+    compare(o, l, ref_o, ref_l, requests=keep, tag="in-launch, earlier stale page")
