@@ -83,7 +83,7 @@ def copy_probe(nbytes, steps):
 
 # the sources the FP8 decode kernel is compiled from (host-side planning and
 # the other kernels do not change its traffic)
-KERNEL_SOURCES = ("mla_decode_fp8.hip", "decode_tile.h", "device_common.h", "launch.h")
+KERNEL_SOURCES = ("mla_decode_fp8.hip", "decode_tile.h", "device_common.h", "launch.h", "page_check.h")
 
 
 def kernel_source_hash():
