@@ -269,3 +269,51 @@ def test_in_launch_check_with_an_earlier_stale_page():
     keep = [0, 2, 3]
     ref_o, ref_l = oracle_decode(w, requests=keep)
     compare(o, l, ref_o, ref_l, requests=keep, tag="in-launch, earlier stale page")
+
+
+def test_in_launch_status_matches_oracle():
+    """The check role of the decode launch (512 threads, so a 140k-token request
+    takes two passes) on one planted fault of each kind: status bit for bit as
+    the oracle's, flagged rows 0 / -inf, clean requests as the attention oracle."""
+    import long_context_mla_amd as mla
+
+    w = synth.custom("check_status", B=7, n_q=1, H=16, context_lens=(140000, 300, 5000, 64, 1, 2100, 777),
+                     cache_dtype="fp8", scale_mode="token", seed=21)
+    rng = np.random.default_rng(5)
+    tags = rng.integers(0, 2**32, size=w.num_pages, dtype=np.uint64).astype(np.uint32)
+    bt_h = w.block_table.copy()
+    et = np.where(bt_h >= 0, tags[np.clip(bt_h, 0, w.num_pages - 1)], 0).astype(np.uint32)
+    ep = bt_h.copy()
+    lens = w.seq_lens.copy()
+    tags[bt_h[0, 2100]] ^= np.uint32(3)           # second pass of the 512-thread check
+    bt_h[1, 2] = (bt_h[1, 2] + 1) % w.num_pages   # another page in the map
+    bt_h[2, 40] = w.num_pages + 3                 # outside the pool
+    lens[3] = w.max_blocks * 64 + 5               # length past the map
+    last5 = (int(lens[5]) - 1) // 64
+    tags[bt_h[5, last5]] ^= np.uint32(1 << 30)    # the page the new row goes to
+    want_s, _ = oi.check_pages_ref(tags, bt_h, et, lens, ep)
+    log(f"in-launch status want={want_s.tolist()}")
+    assert want_s.tolist()[:6] == [oi.STALE_TAG, oi.WRONG_PAGE | oi.STALE_TAG, oi.OUT_OF_RANGE | oi.WRONG_PAGE,
+                                   oi.BAD_LEN, 0, oi.STALE_TAG] and want_s[6] == 0
+
+    g = GpuState(w)
+    stale5 = int(bt_h[5, last5])
+    before = g.cache[stale5].clone()
+    g.block_table = _dev(bt_h)
+    g.seq_lens = _dev(lens)
+    npg = int(-(-w.seq_lens.max() // 64))
+    st = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(), g.device,
+                        pages_per_split=16, max_splits=-(-npg // 16), check_mode="launch")
+    out, lse = st(g.q, g.cache, g.kv_scale, g.scale_mode, g.block_table, g.seq_lens, w.softmax_scale,
+                  new_rows=g.new_rows, page_check=(_dev(tags), _dev(et), _dev(ep)))
+    torch.cuda.synchronize()
+    assert st.status.cpu().numpy().tolist() == want_s.tolist()
+    o = bf16_tensor_to_f64(out)
+    l = lse.detach().cpu().double().numpy()
+    for b in range(w.B):
+        if want_s[b]:
+            assert not o[b].any() and np.all(np.isneginf(l[b])), b
+    assert torch.equal(g.cache[stale5], before), "a row was stored into a page that failed the check"
+    keep = [4, 6]
+    ref_o, ref_l = oracle_decode(w, requests=keep)
+    compare(o, l, ref_o, ref_l, requests=keep, tag="in-launch status")
