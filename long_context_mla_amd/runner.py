@@ -68,7 +68,9 @@ class DecodeStep:
             self.side = torch.cuda.Stream(device=device)
 
     def check(self, page_tags, block_table, expected_tags, seq_lens, expected_pages=None, stream=None):
-        """kv_check_pages into this step's status / checked_lens; returns checked_lens."""
+        """kv_check_pages into this step's status / checked_lens; returns checked_lens.
+        (The in-launch placement writes ``status`` only; ``checked_lens`` then keeps
+        whatever an earlier check left there.)"""
         self._check_buffers(block_table.device)
         _lib.kv_check_pages(page_tags, block_table, expected_tags, seq_lens, self.status,
                             self.checked_lens, expected_pages, stream=stream)
