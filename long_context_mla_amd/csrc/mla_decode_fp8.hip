@@ -301,8 +301,9 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
           // that is in the pool, is the recorded one and carries its tag
           const int64_t e = bt_row + pos / kPage;
           const int raw = load_const(a.block_table, e);
+          const uint32_t cur = load_const(a.page_tags, min(max(raw, 0), a.num_pages - 1));
           store = raw >= 0 && raw < a.num_pages && raw == load_const(a.expected_pages, e) &&
-                  load_const(a.page_tags, raw) == load_const(a.expected_tags, e);
+                  cur == load_const(a.expected_tags, e);
         }
         if (store) {
           const int pg = min(max(load_const(a.block_table, bt_row + pos / kPage), 0), a.num_pages - 1);
