@@ -270,8 +270,9 @@ int mla_decode_plan_lens(const int32_t* seq_lens, int B, int n_q, int H, int num
   // Estimated duration of a plan, in page times.  Workgroup i goes to XCD
   // i % 8 and waits there for the first of its num_cus / 8 compute units to
   // come free (one workgroup per unit at a time); it costs its pages plus a
-  // small fixed start and end.  (Fitted on the box: with this model the plan
-  // it ranks first was the fastest measured on every batched workload.)
+  // small fixed start and end.  (Fitted by measurement on MI355X: with this
+  // model the plan it ranks first was the fastest measured on every batched
+  // workload.)
   constexpr int64_t kFixedPages = 2;
   const int per_xcd = std::max(1, num_cus / 8);
   auto makespan = [&](int pps) {
