@@ -287,7 +287,7 @@ def main():
     pps = args.pages_per_split or None
     ms = args.max_splits or None
     step = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(), dev,
-                          pages_per_split=pps, max_splits=ms, seq_lens_host=w.seq_lens)
+                          pages_per_split=pps, max_splits=ms, seq_lens_host=w.seq_lens, cache_dtype=w.cache_dtype)
     stream = torch.cuda.current_stream()
 
     def run(i, ev=None, st=None, lens=None):

@@ -39,9 +39,11 @@
  * Errors: host-detectable argument errors return a non-zero mla_status_t
  * before anything is launched.  A failed launch returns MLA_ERR_HIP.  No
  * exception or abort crosses the ABI.  Device-side contents (page ids,
- * lengths) are not checked on the host: page ids outside [0, num_pages) are
- * clamped into range and lengths are clamped to [0, max_blocks * 64], so a bad
- * table gives wrong numbers but never an out-of-bounds access.
+ * lengths) are not checked on the host: for reads, page ids outside
+ * [0, num_pages) are clamped into range and lengths are clamped to
+ * [0, max_blocks * 64], so a bad table gives wrong numbers but never an
+ * out-of-bounds access; a new row whose page id is outside [0, num_pages) is
+ * not written anywhere (a clamped id would name another request's page).
  */
 #ifndef MLA_DECODE_H
 #define MLA_DECODE_H
@@ -98,7 +100,8 @@ typedef enum {
  * PER_TOKEN: amax = max_d |x_d|; scale = fp32(amax / 448) (1.0 when amax = 0);
  * code_d = E4M3(fp32(x_d / scale)).  PER_TENSOR: code_d = E4M3(fp32(x_d / kv_scale[0])).
  * Divisions are correctly rounded fp32; E4M3() rounds to nearest, ties to the
- * even code, saturating to +-448.  Positions p < 0 are skipped.
+ * even code, saturating to +-448.  Positions p < 0 or p >= max_blocks * 64,
+ * and rows whose page id is outside [0, num_pages), are skipped.
  * B = 0 or n_new = 0 is a no-op.
  */
 int kv_append_fp8(const void* kv_new, void* kv_cache, float* kv_scale, int scale_mode,
@@ -117,6 +120,7 @@ int kv_append_fp8(const void* kv_new, void* kv_cache, float* kv_scale, int scale
  *   pages_per_split, max_splits  the split-KV plan (mla_decode_plan gives one):
  *               split s of request b covers pages [s*pps, (s+1)*pps), except
  *               that split max_splits-1 also takes every page after it.
+ *               pages_per_split * max_splits must not exceed 2^31 - 1.
  *   o_partial   bf16 [B, max_splits, n_q, H, 512]: per-split output,
  *               normalised by the split's own softmax sum (rounded to bf16:
  *               the partials are read back once, and their rounding is far
@@ -233,15 +237,17 @@ int mla_decode_combine(const void* o_partial, const float* lse_partial, const in
  * mla_decode_plan — host-only helper that picks pages_per_split and max_splits
  * so the split workgroups fill `num_cus` compute units (0 = 256) with about
  * equal work.  max_seq_len and total_seq_len are the largest and the summed
- * L_b of the batch.  Writes *pages_per_split >= 1 and *max_splits >= 1.
- * Touches no device.
+ * L_b of the batch; cache_dtype (mla_cache_dtype_t) selects the kernel the
+ * plan is for (64 query rows per workgroup on FP8, 32 on BF16).  Writes
+ * *pages_per_split >= 1 and *max_splits >= 1.  Touches no device.
  */
 int mla_decode_plan(int B, int n_q, int H, int max_seq_len, int64_t total_seq_len, int num_cus,
-                    int* pages_per_split, int* max_splits);
+                    int cache_dtype, int* pages_per_split, int* max_splits);
 
 /*
  * mla_decode_plan_lens — host-only split plan from the batch's lengths.
  *   seq_lens   host int32 [B], the L_b of the coming launch (after its append).
+ *   cache_dtype  mla_cache_dtype_t of the coming launch.
  * Chooses pages_per_split among the smallest values whose workgroups fit one,
  * two, three or four rounds of `num_cus` compute units (0 = 256), by the
  * shortest estimated duration when workgroup i waits for a free compute unit
@@ -251,7 +257,7 @@ int mla_decode_plan(int B, int n_q, int H, int max_seq_len, int64_t total_seq_le
  * seq_lens with B > 0), MLA_ERR_BAD_SHAPE for a negative length or a plan
  * whose grid would exceed 2^31 - 1 workgroups.  Touches no device.
  */
-int mla_decode_plan_lens(const int32_t* seq_lens, int B, int n_q, int H, int num_cus,
+int mla_decode_plan_lens(const int32_t* seq_lens, int B, int n_q, int H, int num_cus, int cache_dtype,
                          int* pages_per_split, int* max_splits);
 
 /*

@@ -51,8 +51,8 @@ def _load() -> ctypes.CDLL:
     lib.mla_decode_paged.argtypes = [P, P, I, P, I, P, P, I, I, I, I, I, F, I, I, P, P, P, P, P]
     lib.mla_decode_combine.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, P]
     lib.mla_decode_paged_append.argtypes = [P, I, P, P, P, I, P, P, I, I, I, I, I, F, I, I, P, P, P, P, I, P]
-    lib.mla_decode_plan.argtypes = [I, I, I, I, L, I, ctypes.POINTER(I), ctypes.POINTER(I)]
-    lib.mla_decode_plan_lens.argtypes = [P, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
+    lib.mla_decode_plan.argtypes = [I, I, I, I, L, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
+    lib.mla_decode_plan_lens.argtypes = [P, I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
     lib.kv_check_pages.argtypes = [P, I, P, P, P, P, I, I, P, P, P]
     lib.mla_decode_paged_append_checked.argtypes = [P, I, P, P, P, I, P, P, I, I, I, I, I, F, I, I, P, P,
                                                     P, P, P, P, P]
@@ -164,6 +164,10 @@ def mla_decode_paged(q, kv_cache, kv_scale, scale_mode, block_table, seq_lens, s
         raise ValueError("block_table / seq_lens batch mismatch")
     if mode != SCALE_NONE:
         _need(kv_scale, "kv_scale", torch.float32, dev)
+        if mode == SCALE_PER_TOKEN and tuple(kv_scale.shape) != (num_pages, PAGE_SIZE):
+            raise ValueError("per-token kv_scale must be [num_pages, 64]")
+        if mode == SCALE_PER_TENSOR and kv_scale.numel() != 1:
+            raise ValueError("per-tensor kv_scale must have one element")
     if max_splits == 1:
         _need(out, "out", torch.bfloat16, dev)
         _need(lse, "lse", torch.float32, dev)
@@ -256,24 +260,31 @@ def mla_decode_combine(o_partial, lse_partial, seq_lens, max_blocks, pages_per_s
         int(pages_per_split), max_splits, _ptr(out), _ptr(lse), _ptr(status), _stream(stream)))
 
 
-def mla_decode_plan_lens(seq_lens, n_q, H, num_cus=0):
-    """Host-only split plan from the batch's lengths (a host sequence of ints):
-    returns (pages_per_split, max_splits)."""
+def _dtype_code(cache_dtype):
+    if isinstance(cache_dtype, str):
+        return {"fp8": CACHE_FP8_E4M3, "bf16": CACHE_BF16}[cache_dtype]
+    return int(cache_dtype)
+
+
+def mla_decode_plan_lens(seq_lens, n_q, H, num_cus=0, cache_dtype="fp8"):
+    """Host-only split plan from the batch's lengths (a host sequence of ints)
+    for a cache of `cache_dtype` ("fp8" / "bf16" or CACHE_*): returns
+    (pages_per_split, max_splits)."""
     import numpy as np
 
     lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32).reshape(-1))
     pps, ms = ctypes.c_int(0), ctypes.c_int(0)
     _check("mla_decode_plan_lens", LIB.mla_decode_plan_lens(
         lens.ctypes.data if lens.size else None, int(lens.size), int(n_q), int(H), int(num_cus),
-        ctypes.byref(pps), ctypes.byref(ms)))
+        _dtype_code(cache_dtype), ctypes.byref(pps), ctypes.byref(ms)))
     return pps.value, ms.value
 
 
-def mla_decode_plan(B, n_q, H, max_seq_len, total_seq_len, num_cus=0):
+def mla_decode_plan(B, n_q, H, max_seq_len, total_seq_len, num_cus=0, cache_dtype="fp8"):
     """Host-only split plan: returns (pages_per_split, max_splits)."""
     pps, ms = ctypes.c_int(0), ctypes.c_int(0)
     _check("mla_decode_plan", LIB.mla_decode_plan(int(B), int(n_q), int(H), int(max_seq_len),
-                                                  int(total_seq_len), int(num_cus),
+                                                  int(total_seq_len), int(num_cus), _dtype_code(cache_dtype),
                                                   ctypes.byref(pps), ctypes.byref(ms)))
     return pps.value, ms.value
 

@@ -15,6 +15,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_decode.so")
 SOURCES = ["api.hip", "kv_append.hip", "mla_decode.hip", "mla_decode_fp8.hip", "mla_combine.hip", "kv_check.hip"]
+# measured-peak microbenchmarks (bench.py --peaks): a library of their own
+PEAKS_LIB = os.path.join(HERE, "libmla_peaks.so")
+PEAKS_SOURCES = ["peaks.hip"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -37,8 +40,8 @@ def hipcc() -> str:
     return p
 
 
-def build(extra_flags=(), verbose: bool = False, out: str = LIB) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+def build(extra_flags=(), verbose: bool = False, out: str = LIB, sources=None) -> str:
+    srcs = [os.path.join(CSRC, s) for s in (SOURCES if sources is None else sources)]
     tmp = out + ".tmp"
     cmd = [hipcc(), *FLAGS, *extra_flags, "-o", tmp, *srcs]
     if verbose:
@@ -52,5 +55,9 @@ def build(extra_flags=(), verbose: bool = False, out: str = LIB) -> str:
     return out
 
 
+def build_all(verbose: bool = False) -> list:
+    return [build(verbose=verbose), build(verbose=verbose, out=PEAKS_LIB, sources=PEAKS_SOURCES)]
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build_all(verbose=True))

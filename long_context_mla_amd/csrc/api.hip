@@ -40,9 +40,11 @@ int decode_impl(const void* q, const void* kv_cache, int cache_dtype, const floa
   if (bad_stream_free_shape(B, n_q, H)) return MLA_ERR_BAD_SHAPE;
   if (max_blocks < 1 || num_pages < 1 || pages_per_split < 1 || max_splits < 1) return MLA_ERR_BAD_SHAPE;
   if ((int64_t)max_blocks * MLA_PAGE_SIZE > 2147483647LL) return MLA_ERR_BAD_SHAPE;
+  // split starts s * pages_per_split stay inside int
+  if ((int64_t)pages_per_split * max_splits > 2147483647LL) return MLA_ERR_BAD_SHAPE;
   if (!std::isfinite(softmax_scale)) return MLA_ERR_BAD_SHAPE;
   const int R = n_q * H;
-  const int rows = mla::decode_rows_per_group(B, R);
+  const int rows = mla::decode_rows_per_group(cache_dtype == MLA_CACHE_FP8_E4M3 ? mla::kFp8 : mla::kBf16);
   const int n_rg = (R + rows - 1) / rows;
   if (mla::decode_grid_size(B, max_splits, n_rg) + (status ? B : 0) > kMaxGrid) return MLA_ERR_BAD_SHAPE;
   if (B == 0) return MLA_OK;
@@ -194,6 +196,7 @@ int mla_decode_combine(const void* o_partial, const float* lse_partial, const in
                        void* out, float* lse, const int32_t* status, void* stream) {
   if (bad_stream_free_shape(B, n_q, H)) return MLA_ERR_BAD_SHAPE;
   if (max_blocks < 1 || pages_per_split < 1 || max_splits < 1) return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)pages_per_split * max_splits > 2147483647LL) return MLA_ERR_BAD_SHAPE;
   if ((int64_t)B * n_q * H * 4 > kMaxGrid) return MLA_ERR_BAD_SHAPE;
   if (B == 0) return MLA_OK;
   if (!o_partial || !lse_partial || !seq_lens || !out || !lse) return MLA_ERR_NULL_PTR;
@@ -214,13 +217,14 @@ int mla_decode_combine(const void* o_partial, const float* lse_partial, const in
 }
 
 int mla_decode_plan(int B, int n_q, int H, int max_seq_len, int64_t total_seq_len, int num_cus,
-                    int* pages_per_split, int* max_splits) {
+                    int cache_dtype, int* pages_per_split, int* max_splits) {
   if (!pages_per_split || !max_splits) return MLA_ERR_NULL_PTR;
   if (bad_stream_free_shape(B, n_q, H) || max_seq_len < 0 || total_seq_len < 0 || num_cus < 0)
     return MLA_ERR_BAD_SHAPE;
+  if (cache_dtype != MLA_CACHE_BF16 && cache_dtype != MLA_CACHE_FP8_E4M3) return MLA_ERR_UNSUPPORTED;
   if (num_cus == 0) num_cus = 256;
   const int R = n_q * H;
-  const int rows = mla::decode_rows_per_group(B, R);
+  const int rows = mla::decode_rows_per_group(cache_dtype == MLA_CACHE_FP8_E4M3 ? mla::kFp8 : mla::kBf16);
   const int64_t n_rg = (R + rows - 1) / rows;
   const int64_t max_pages = (max_seq_len + MLA_PAGE_SIZE - 1) / MLA_PAGE_SIZE;
   // pages of the batch, counting a partial last page per request
@@ -241,13 +245,15 @@ int mla_decode_plan(int B, int n_q, int H, int max_seq_len, int64_t total_seq_le
   return MLA_OK;
 }
 
-int mla_decode_plan_lens(const int32_t* seq_lens, int B, int n_q, int H, int num_cus,
+int mla_decode_plan_lens(const int32_t* seq_lens, int B, int n_q, int H, int num_cus, int cache_dtype,
                          int* pages_per_split, int* max_splits) {
   if (!pages_per_split || !max_splits || (B > 0 && !seq_lens)) return MLA_ERR_NULL_PTR;
   if (bad_stream_free_shape(B, n_q, H) || num_cus < 0) return MLA_ERR_BAD_SHAPE;
+  if (cache_dtype != MLA_CACHE_BF16 && cache_dtype != MLA_CACHE_FP8_E4M3) return MLA_ERR_UNSUPPORTED;
   if (num_cus == 0) num_cus = 256;
   const int R = n_q * H;
-  const int n_rg = (R + mla::decode_rows_per_group(B, R) - 1) / mla::decode_rows_per_group(B, R);
+  const int rows = mla::decode_rows_per_group(cache_dtype == MLA_CACHE_FP8_E4M3 ? mla::kFp8 : mla::kBf16);
+  const int n_rg = (R + rows - 1) / rows;
   std::vector<int> pages(B);
   int max_pages = 0;
   for (int b = 0; b < B; ++b) {

@@ -270,6 +270,11 @@ __device__ __forceinline__ void mfma_drain_o(f32x4 (&o)[2][8], bf16x8 a0, bf16x8
 __device__ __forceinline__ void mfma_drain_s(f32x4& s0, f32x4& s1, bf16x8 a) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1) : "v"(a));
 }
+// The same hold without the wait: for the second half of a group whose first
+// half's drain has already waited out the pipe.
+__device__ __forceinline__ void mfma_tie_o(f32x4 (&o)[2][8], bf16x8 a0, bf16x8 a1, bf16x8 b) {
+  asm volatile("" : MLA_O16(o) : "v"(a0), "v"(a1), "v"(b));
+}
 // Result fence alone on the sixteen P V accumulators.
 __device__ __forceinline__ void mfma_result_fence_v16(f32x4 (&o)[2][8]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : MLA_O16(o));
@@ -295,6 +300,28 @@ __device__ __forceinline__ void mfma_zero_o(f32x4 (&o)[2][8]) {
       : MLA_O16(o)
       : "v"(z));
 }
+// The same, defining the accumulators afresh (write-only operands): where the
+// accumulators are zeroed at the top of a loop, no copy of their previous
+// values has to be kept across the loop's back edge.
+#define MLA_O16_DEF(o) "=&v"(o[0][0]), "=&v"(o[0][1]), "=&v"(o[0][2]), "=&v"(o[0][3]), "=&v"(o[0][4]), \
+    "=&v"(o[0][5]), "=&v"(o[0][6]), "=&v"(o[0][7]), "=&v"(o[1][0]), "=&v"(o[1][1]), "=&v"(o[1][2]),      \
+    "=&v"(o[1][3]), "=&v"(o[1][4]), "=&v"(o[1][5]), "=&v"(o[1][6]), "=&v"(o[1][7])
+__device__ __forceinline__ void mfma_def_zero_o(f32x4 (&o)[2][8]) {
+  const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %1, %16, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %3, %16, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %4, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %5, %16, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %6, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %7, %16, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %8, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %9, %16, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %10, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %11, %16, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %12, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %13, %16, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %14, %16, %16, 0\n\tv_mfma_f32_16x16x32_bf16 %15, %16, %16, 0\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : MLA_O16_DEF(o)
+      : "v"(z));
+}
 __device__ __forceinline__ bf16x8 bf16x8_of(const uint32_t (&d)[4]) {
   return __builtin_bit_cast(bf16x8, u32x4{d[0], d[1], d[2], d[3]});
 }
@@ -315,6 +342,26 @@ __device__ __forceinline__ f32x4 mfma_zero() {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(z, z, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 }
 
+// 32 x 32 x 16 bf16 MFMAs on a 16-register accumulator (VGPRs), the same
+// hand-placed conventions: "_w" forms wait out a VALU write of a source just
+// before, "first" forms start a chain from 0, and the drain waits out the
+// result latency while holding the last operands.
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+__device__ __forceinline__ void mfma32_w(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_first(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_first_w(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_drain(f32x16& c0, f32x16& c1, bf16x8 a) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c0), "+v"(c1) : "v"(a));
+}
 __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

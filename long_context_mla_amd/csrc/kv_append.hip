@@ -16,8 +16,10 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendArgs a) {
   const int lane = threadIdx.x;
   const int pos = a.seq_lens[b] - a.n_new + j;
   if (pos < 0 || pos >= a.max_blocks * kPage) return;
-  int page = a.block_table[(int64_t)b * a.max_blocks + pos / kPage];
-  page = min(max(page, 0), a.num_pages - 1);
+  // a page id outside the pool names no page: nothing is written (clamping it
+  // would put the row into another request's page)
+  const int page = a.block_table[(int64_t)b * a.max_blocks + pos / kPage];
+  if (page < 0 || page >= a.num_pages) return;
   const int slot = pos % kPage;
 
   u32x2 codes[2];

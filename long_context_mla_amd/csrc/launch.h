@@ -67,8 +67,10 @@ struct CombineArgs {
   int B, R, max_blocks, pps, max_splits;
 };
 
-// Rows of the query matrix one decode workgroup owns (32 or 64).
-int decode_rows_per_group(int B, int R);
+// Rows of the query matrix one decode workgroup owns: 64 on an FP8 cache
+// (decode_rows_fp8), 32 on a BF16 cache.
+int decode_rows_per_group(int cache_kind);
+int decode_rows_fp8();
 
 // Workgroups of a decode launch (a 1-D grid): the B * max_splits work units
 // (request, split) padded to a multiple of the 8 XCDs, n_rg row groups each.

@@ -452,15 +452,12 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     }
 }
 
-int decode_rows_per_group(int B, int R) {
-  (void)B;
-  (void)R;
-  return kRows;
-}
+int decode_rows_per_group(int cache_kind) { return cache_kind == kFp8 ? decode_rows_fp8() : kRows; }
 
 hipError_t launch_decode(const DecodeArgs& a0, int cache_kind, int scale_mode, hipStream_t stream) {
   DecodeArgs a = a0;
-  a.n_rg = (a.R + kRows - 1) / kRows;
+  const int rows = decode_rows_per_group(cache_kind);
+  a.n_rg = (a.R + rows - 1) / rows;
   if (cache_kind == kFp8) return launch_decode_fp8(a, scale_mode, stream);
   const dim3 grid((unsigned)decode_grid_size(a.B, a.max_splits, a.n_rg)), block(256);
   hipLaunchKernelGGL(decode_bf16_kernel, grid, block, 0, stream, a);

@@ -7,29 +7,35 @@
 // safer: running Kimi and GLM at scale", section "Quantizing the KV cache").
 //
 // gfx950 design: one 512-thread workgroup (8 waves, two per SIMD) per
-// (request, split, group of 32 query rows), one per CU.  The two waves of a
-// SIMD do different work on different pages, so that one's stalls (LDS
-// latency, conversions, the softmax) are covered by the other's MFMAs:
-//  * score waves 0..3: wave w copies tokens 16w..16w+15 of each page HBM ->
-//    LDS (LDS-DMA), computes their scores S^T = K Q^T for all 32 rows
-//    (query held in VGPRs), the softmax weights P (bf16, into LDS) and the sums;
-//  * output waves 4..7: wave 4+j accumulates O[32 rows][128j .. 128j+127] +=
+// (request, split, group of 64 query rows), one per CU.  64 rows cover every
+// head of one query token of the 64-head models, so each page of a split is
+// fetched into LDS once per compute unit: the per-unit fetch rate, not HBM,
+// caps a page stream on this chip (about 30 GB/s per unit by LDS-DMA), and
+// a page read by two 32-row workgroups costs its units twice the bytes.
+//  * score waves 0..3: wave w = 2*th + rh holds the query of rows
+//    32rh .. 32rh+31 in VGPRs (bf16 MFMA operands) and computes S^T = K Q^T for
+//    tokens 32th .. 32th+31 of each page, the softmax weights P (bf16, into
+//    LDS) and the sums;
+//  * output waves 4..7: wave 4+j accumulates O[64 rows][128j .. 128j+127] +=
 //    P V over the previous page, V being the first 512 columns of the same
-//    staged rows (transposing LDS reads).
+//    staged rows (transposing LDS reads), and copies quarter j (tokens
+//    16j .. 16j+15) of every page HBM -> LDS by LDS-DMA, two pages ahead.
 // One barrier per page separates "scores of page p" from "P V of page p".
-// The two roles run separate loops with the same sequence of barriers, so the
-// query (score waves) and the accumulators (output waves) never need registers
-// at the same time.  Two waves per SIMD leave 256 registers per wave; the
-// kernel uses VGPRs only (no AGPRs), so all 256 are available to either role.
+//
+// LDS: the V parts (first 512 bytes of each row) of four pages, the rope parts
+// (last 64 bytes) of three (rope bytes are dead once the scores of their page
+// are done, a page before its V bytes), P of two pages, and small arrays.
 //
 // mla_decode_paged_append runs the same kernel with the step's new rows: the
-// score wave that owns a new row's slot encodes it into its LDS copy of the
+// output wave that copies a new row's slot encodes it into its LDS copy of the
 // page (as kv_append_fp8 would), and row group 0 writes it to the cache.
 //
 // Softmax: one fixed reference per row and split (the first page's maximum),
-// weights 2^(y - m0); a weight above 2^64 restarts the split with a larger
-// reference (all waves together).  The output divides by the sum of the bf16
-// weights that P V used; the LSE uses the exact fp32 sum.
+// weights 2^(y - m0).  A weight above 2^64 switches the split to a scan: the
+// remaining pages are scored (no weights, no P V) to find every row's maximum,
+// and the split runs once more with that maximum as its reference, which no
+// score can exceed.  The output divides by the sum of the bf16 weights that
+// P V used; the LSE uses the exact fp32 sum.
 #include <type_traits>
 
 #include "decode_tile.h"
@@ -39,33 +45,68 @@
 
 namespace mla {
 
-// CHECKED: the launch also carries the page-tag check (a.status != null).
+namespace {
+
+constexpr int kRows8 = 64;       // query rows per workgroup
+constexpr int kVBuf = 4;         // staged V parts (pages)
+constexpr int kRBuf = 3;         // staged rope parts (pages)
+constexpr int kVBytes = 32768;   // V part of a page: 64 tokens x 512 bytes
+constexpr int kRBytes = 4096;    // rope part: 64 tokens x 64 bytes
+constexpr int kPBytes = kRows8 * 128;  // P of a page: 64 rows x 64 tokens bf16
+constexpr int kLoads = 9;        // 1 KB LDS-DMA loads per output wave per page (8 V + 1 rope)
+
+// LDS map (bytes)
+constexpr int kOffV = 0;
+constexpr int kOffR = kOffV + kVBuf * kVBytes;      // 131072
+constexpr int kOffP = kOffR + kRBuf * kRBytes;      // 143360
+constexpr int kOffScale = kOffP + 2 * kPBytes;      // 159744: fp32 [4][64]
+constexpr int kOffRed = kOffScale + kVBuf * 256;    // 160768: fp32 [2][64]
+constexpr int kOffLsum = kOffRed + 512;             // fp32 [2][64]
+constexpr int kOffLnrm = kOffLsum + 512;            // fp32 [2][64]
+constexpr int kOffM0 = kOffLnrm + 512;              // fp32 [64]
+constexpr int kOffFlag = kOffM0 + 256;              // uint32 [2]
+constexpr int kLdsBytes = kOffFlag + 16;
+// The query of the group's 64 rows (73,728 bytes) is staged once at the start
+// over buffers that stay free until page 2's copy: rows 0..55 over V buffers
+// 2 and 3, rows 56..63 over rope buffer 2 and P buffer 0.
+constexpr int kQA = kOffV + 2 * kVBytes;            // 65536: 56 rows
+constexpr int kQB = kOffR + 2 * kRBytes;            // 139264: 8 rows
+constexpr int kQRowBytes = kD * 2;                  // 1152
+static_assert(kQA + 56 * kQRowBytes <= kOffR && kQB + 8 * kQRowBytes <= kOffP + kPBytes, "query staging");
+constexpr int kQLoads = 18;                         // 1 KB query copies per score wave (72 in all)
+static_assert(kLdsBytes <= 163840, "LDS");
+static_assert(4 * kRows8 * 272 <= kOffP, "the output tiles fit over the page buffers");
+
+// Staged page layout.  Token t = 16q + m (quarter q, m < 16), 16-byte chunk c
+// of its 576-byte row (36 per row): chunks c < 32 (the V part) sit in V-buffer
+// slot q*512 + (c/4)*64 + 4m + ((c%4) ^ F), chunks 32..35 in rope-buffer slot
+// q*64 + 4m + ((c%4) ^ F), with F = (m/4) ^ (2 (q%2)).  Then
+//  * one LDS-DMA instruction fills one group of 64 slots: lane l brings token
+//    16q + l/4, chunk 4i + ((l%4) ^ F) (one source offset per lane for all
+//    nine groups of its quarter);
+//  * the QK^T operand reads (16 tokens x one 16-byte chunk each 16 lanes)
+//    and the transposing P V reads (8-byte halves of one chunk of tokens
+//    4g..4g+3 and 16+4g..16+4g+3 of a 32-token block, 32 lanes per access)
+//    hit distinct banks.
+__device__ __forceinline__ int swz(int m4, int q) { return m4 ^ ((q & 1) << 1); }
+
+// Keeps the compiler from moving memory accesses across this point (no
+// instruction): it stops loads of a later phase from being hoisted over the
+// MFMAs of an earlier one, where their registers would be live at once.
+__device__ __forceinline__ void phase_fence() { asm volatile("" ::: "memory"); }
+
 template <int SCALE, bool CHECKED>
 __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
-  using T = Tile<kFp8>;
-  // LDS layout of a staged page (36 16-byte chunks per token): token t's
-  // chunk c sits in 16-byte slot pslot(t, c).  Each 16-token quarter (the
-  // tokens one score wave copies and reads) takes 576 consecutive slots, in
-  // nine groups of 64: group c / 4 holds chunks 4(c / 4) .. +3 of the 16
-  // tokens, four per token, the chunk's two low bits XORed with
-  // F(t % 16) = {0, 2, 3, 1}[(t % 16) / 4].  One page copy instruction then
-  // fills one group (lane l: token l / 4, chunk (l % 4) ^ F), and both the
-  // QK^T operand reads (16 B: token, chunk) and the transposing P V reads
-  // (8 B: 8 tokens of one chunk) hit distinct LDS banks.
-  auto pswz = [](int tl) { return (0x78 >> (2 * ((tl >> 2) & 3))) & 3; };
-  auto pslot = [&](int t, int c) {
-    const int tl = t & 15;
-    return (t >> 4) * 576 + (c >> 2) * 64 + tl * 4 + ((c & 3) ^ pswz(tl));
-  };
-  static_assert(T::NBUF == 4 && T::DIST == 2, "four page buffers, two pages in flight");
-  __shared__ __attribute__((aligned(16))) uint8_t s_kv[T::NBUF][T::PAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) float s_scale[T::NBUF][kPage];
-  __shared__ __attribute__((aligned(16))) uint8_t s_p[2][kRows * T::PSTRIDE];
-  __shared__ float s_red[4][kRows];   // per-score-wave row maxima (first page, restarts)
-  __shared__ float s_lsum[4][kRows];
-  __shared__ float s_lnrm[4][kRows];
-  __shared__ float s_m0[kRows];
-  __shared__ __attribute__((aligned(16))) uint8_t s_flag[2][4];  // [page parity][score wave]
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  uint8_t* const s_v = lds + kOffV;
+  uint8_t* const s_rope = lds + kOffR;
+  uint8_t* const s_p = lds + kOffP;
+  float* const s_scale = reinterpret_cast<float*>(lds + kOffScale);
+  float* const s_red = reinterpret_cast<float*>(lds + kOffRed);
+  float* const s_lsum = reinterpret_cast<float*>(lds + kOffLsum);
+  float* const s_lnrm = reinterpret_cast<float*>(lds + kOffLnrm);
+  float* const s_m0 = reinterpret_cast<float*>(lds + kOffM0);
+  uint8_t* const s_flag = lds + kOffFlag;  // [page parity][score wave], one byte each
 
   // Workgroups past the decode's carry the page-tag check, one per request.
   // The attention above does not wait for them: flagged requests are masked
@@ -84,64 +125,61 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     c.max_blocks = a.max_blocks;
     c.num_pages = a.num_pages;
     const int cb = (int)blockIdx.x - a.check_from;
-    const int st = check_request<512>(c, cb, a.seq_lens[cb], reinterpret_cast<int*>(&s_red[0][0]));
+    const int st = check_request<512>(c, cb, a.seq_lens[cb], reinterpret_cast<int*>(s_red));
     if (threadIdx.x == 0) a.status[cb] = st;
     return;
   }
 
-  // One round trip for the launch arguments the first loads need: without
-  // this the compiler fetches them in dependent batches.
+  // One round trip for the launch arguments the first loads need.
   asm volatile("" :: "s"(a.q), "s"(a.block_table), "s"(a.seq_lens), "s"(a.n_rg), "s"(a.max_blocks));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool scorer = wave < 4;
-  const int qw = wave & 3;  // index within the role
   const int m = lane & 15, g = lane >> 4;
   const WorkUnit wu = decode_work_unit(a.B, a.max_splits, a.n_rg);
   if (!wu.valid) return;
   const int b = wu.b, split = wu.split, rg = wu.rg;
-  const int r0 = rg * kRows;
+  const int r0 = rg * kRows8;
   const int p_begin = split * a.pps;
   const int64_t bt_row = (int64_t)b * a.max_blocks;
-  constexpr int QBUF = T::NBUF - 1;
-  constexpr int kQueryLoads = 9;  // 16-byte query copies per score wave (32 rows x 1,152 B / 4 waves)
+  const int cap = a.max_blocks * kPage;
 
-  // Before anything waits, the score waves issue the two loads that depend on
-  // the launch arguments alone, so that their latencies overlap the length's:
-  //  * the split's first 64 page ids (bounded by the table row, not yet by the
-  //    length), one per lane;
-  //  * the query of the group's 32 rows, HBM -> LDS in one coalesced copy
-  //    shared by the four score waves, into the page buffer that stays free
-  //    until the third page copy.  Row r's 16-byte chunk c (72 per row) goes to
-  //    slot r * 72 + (c ^ ((r / 2) % 8)), which makes the operand reads below
-  //    free of bank conflicts.  Rows past R repeat row R - 1 (results dropped).
-  // Every load of page ids is inline asm, awaited explicitly with the result
-  // tied to the wait: a load the compiler tracks would make it wait for all
-  // copies in flight before each later readlane of the ids.
+  // The output waves' first 64 page ids of the split go out before the length
+  // is known (bounded by the table row, not yet by the length), one per lane,
+  // so that their latency overlaps the length's.
   int ids = 0;
-  if (scorer) {
+  const int rh = wave & 1, th = (wave >> 1) & 1;
+  if (!scorer) {
     const int32_t* id_src = a.block_table + bt_row + min(p_begin + lane, a.max_blocks - 1);
     asm volatile("global_load_dword %0, %1, off" : "=v"(ids) : "v"(id_src) : "memory");
-    const uint16_t* qbase = a.q + ((int64_t)b * a.R + r0) * kD;
-    const int rmax = a.R - 1 - r0;
-    const uint32_t qlds = lds_addr(&s_kv[QBUF][0]);
+  } else {
+    // The score waves copy the query of the group's 64 rows HBM -> LDS in 72
+    // coalesced 1 KB LDS-DMA copies (the rows are contiguous in q): slot s
+    // (16 bytes) of the staged query is row s / 72, chunk (s % 72) ^ ((row / 2) % 8),
+    // which makes the operand reads below free of bank conflicts.  Rows past R
+    // repeat row R - 1.
+    const uint8_t* qbase = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * a.R * kD);
 #pragma unroll
-    for (int j = 0; j < kQueryLoads; ++j) {
-      const int slot = (qw * 9 + j) * 64 + lane;  // 2304 slots = 32 rows x 72 chunks
-      const int r = slot / 72;
-      const int c = (slot - r * 72) ^ ((r >> 1) & 7);
-      lds_dma16(qbase, (uint32_t)(min(r, rmax) * (kD * 2) + c * 16), qlds + (qw * 9 + j) * 1024);
+    for (int k = 0; k < kQLoads; ++k) {
+      const int ii = kQLoads * wave + k;
+      const int sl = ii * 64 + lane;
+      const int r = sl / 72;
+      const int c = (sl - r * 72) ^ ((r >> 1) & 7);
+      const uint32_t dst = lds_addr(lds + (ii < 63 ? kQA + ii * 1024 : kQB + (ii - 63) * 1024));
+      lds_dma16(qbase, (uint32_t)(min(r0 + r, a.R - 1) * kQRowBytes + c * 16), dst);
     }
   }
-  const int L = min(max(load_const(a.seq_lens, b), 0), a.max_blocks * kPage);
+  const int L_raw = load_const(a.seq_lens, b);
+  const int L = min(max(L_raw, 0), cap);
   const int n_pages = (L + kPage - 1) / kPage;
 
   if (p_begin >= n_pages) {
     // Nothing to read.  Only an empty request's first split reports it; the
-    // combine never reads splits past a request's last page.
-    if (scorer) wait_vmcnt<0>();  // the query copy lands before the workgroup ends
+    // combine never reads splits past a request's last page.  (Every copy
+    // lands before the workgroup ends.)
+    wait_vmcnt<0>();
     if (n_pages == 0 && split == 0) {
-      for (int e = threadIdx.x; e < kRows * kDV; e += 512) {
+      for (int e = threadIdx.x; e < kRows8 * kDV; e += 512) {
         const int r = r0 + e / kDV;
         if (r >= a.R) break;
         if (a.max_splits == 1)
@@ -149,7 +187,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
         else
           a.o_part[((int64_t)b * a.max_splits * a.R + r) * kDV + e % kDV] = 0;
       }
-      for (int r = r0 + threadIdx.x; r < min(r0 + kRows, a.R); r += 512) {
+      for (int r = r0 + threadIdx.x; r < min(r0 + kRows8, a.R); r += 512) {
         if (a.max_splits == 1)
           a.lse[(int64_t)b * a.R + r] = -INFINITY;
         else
@@ -161,517 +199,506 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   const int p_end = split == a.max_splits - 1 ? n_pages : min(n_pages, p_begin + a.pps);
   const int n_it = p_end - p_begin;
   const float tscale = SCALE == kScaleTensor ? load_const(a.kv_scale, 0) : 1.0f;
-  bool have_ref = false;
-  int restarts = 0;
-  // The four score waves' restart flags of page it, one byte each, read as one
-  // word.  They are read right after the barrier that publishes them and
-  // looked at only after the next block of MFMA work has been issued:
-  // settle() ties the word to that point, so the LDS latency of the read is
-  // not waited for at the barrier.
-  auto flag_words = [&](int it) { return *reinterpret_cast<const uint32_t*>(&s_flag[it & 1][0]); };
+  bool have_ref = false;   // the reference is fixed (first page done, or a rerun)
+  bool allow_scan = true;  // the first run may switch to a scan; the rerun cannot need one
+
+  // The four score waves' overflow flags of page it, one byte each, read as
+  // one word right after the barrier that publishes them and looked at only
+  // after the next block of MFMA work has been issued: settle() ties the word
+  // to that point, so the LDS latency of the read is not waited for at the
+  // barrier.
+  auto flag_word = [&](int it) { return *reinterpret_cast<const uint32_t*>(s_flag + 4 * (it & 1)); };
   auto settle = [](uint32_t& f) {
     asm volatile("" : "+v"(f));
     f = __builtin_amdgcn_readfirstlane(f);  // uniform again for the branch on it
   };
-  auto restart_asked = [&](uint32_t f) { return f != 0u && restarts < kMaxRestarts; };
 
   if (scorer) {
     // =====================================================================
-    // score waves
+    // score waves: rows 32rh .. 32rh+31, tokens 32th .. 32th+31 of each page
     // =====================================================================
+    // QK^T runs on v_mfma_f32_32x32x16_bf16: one 32 x 32 tile is this wave's
+    // 32 tokens x 32 rows, and the 36 k-blocks of 16 dims alternate between two
+    // accumulators (even and odd k-blocks), which keeps the matrix core busy
+    // through the dependent-accumulation latency (about 44 cycles, longer than
+    // one 32-cycle MFMA).  Lane l works on row 32rh + (l % 32) of the query and,
+    // as the K operand, on token 32th + (l % 32) of the page; its k half is
+    // sg = l / 32.  K-block 2p + e holds the dims 32p + 16sg + 8e .. +8 of the
+    // lane: bytes 8e .. 8e+7 of the token's 16-byte chunk 2p + sg, and the
+    // query's 16-byte chunk 4p + 2sg + e.
+    const int sn = lane & 31, sg = lane >> 5;
+    const int lr = 32 * rh + sn;  // this lane's row within the group
+    bf16x8 qop[kD / 16];          // the row's 36 query operands, for the whole split
+    wait_vmcnt<0>();  // this wave's query copies have landed
+    __syncthreads();  // (Q) the query is staged
+    {
+      const uint8_t* qrow = lds + (lr < 56 ? kQA + lr * kQRowBytes : kQB + (lr - 56) * kQRowBytes);
+#pragma unroll
+      for (int kb = 0; kb < kD / 16; ++kb) {
+        const int c = 4 * (kb >> 1) + 2 * sg + (kb & 1);
+        qop[kb] = *reinterpret_cast<const bf16x8*>(qrow + ((c ^ ((lr >> 1) & 7)) << 4));
+      }
+    }
     const float coef = a.sm_log2 * tscale;
-    // Page ids of the split, 64 at a time, one per lane; picked out with
-    // readlane so the DMA issue never waits on a scalar load.  Ids past the
-    // split are never used; every used one is clamped to the pool.  The first
-    // chunk was requested at the start, before the wave's nine query copies:
-    // loads complete in order, so waiting until nine remain waits for the ids
-    // alone and the first pages' copies go out while the query still lands.
-    // Later chunks, and the first again on a restart, wait for themselves.
-    static_assert(kQueryLoads == 9, "the wait below counts the query copies");
-    asm volatile("s_waitcnt vmcnt(9)" : "+v"(ids) :: "memory");
-    int id_chunk = 0;
-    auto reload_ids = [&](int chunk) {
-      id_chunk = chunk;
-      const int32_t* src = a.block_table + bt_row + min(p_begin + (chunk << 6) + lane, p_end - 1);
-      asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(ids) : "v"(src) : "memory");
-    };
-
-    // causal limit of this lane's rows rb*16 + m: row i*H + h sees tokens
-    // t < L - n_q + i + 1; lim_lo is the first token any real row of the group
-    // masks, so earlier pages need no mask (rows past R only pad the group)
-    int lim[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int row = r0 + rb * 16 + m;
-      lim[rb] = row < a.R ? L - a.n_q + row / a.H + 1 : 0;
-    }
+    // causal limit of this lane's row: row i*H + h sees tokens
+    // t < L - n_q + i + 1; lim_lo is the first token any real row of the
+    // workgroup masks, so earlier pages need no mask (rows past R pad the group)
+    const int lim = r0 + lr < a.R ? L - a.n_q + (r0 + lr) / a.H + 1 : 0;
     const int lim_lo = L - a.n_q + r0 / a.H + 1;
-
-    constexpr int LPP = T::LOADS + (SCALE == kScaleToken ? 1 : 0);  // loads per page per wave
-    // wave w copies tokens 16w .. 16w+15 (the rows its own QK^T reads): copy
-    // instruction j fills slot group j of its quarter, lane l taking token
-    // 16w + l/4's chunk 4j + ((l % 4) ^ F), at source byte goff + 64 j
-    static_assert(T::LOADS == 9 && T::ROW_BYTES == 576, "nine copies of 16 tokens x 4 chunks");
-    const uint32_t goff =
-        (uint32_t)((qw * 16 + (lane >> 2)) * T::ROW_BYTES + ((lane & 3) ^ pswz(lane >> 2)) * 16);
-    // Page p_begin + it (and its scales) HBM -> its LDS buffer, two pages
-    // ahead of its use.  dma_page picks the page and copies the scales;
-    // dma_load(j) issues this wave's j-th 16-byte load of it.  Inside the loop
-    // the nine loads ride between the QK^T MFMAs: issued in one burst, the four
-    // score waves' 36 loads back up the CU's address path and stall the wave.
-    const uint8_t* dma_src = a.cache;
-    uint32_t dma_dst = 0;
-    auto dma_page = [&](int it) {
-      if ((it >> 6) != id_chunk) reload_ids(it >> 6);
-      const int pg = min(max(__builtin_amdgcn_readlane(ids, it & 63), 0), a.num_pages - 1);
-      dma_src = a.cache + (int64_t)pg * T::PAGE_BYTES;
-      dma_dst = lds_addr(&s_kv[it % T::NBUF][0]) + qw * T::LOADS * 1024;
-      // the scales of the wave's own 16 tokens only: a row appended in this
-      // launch overwrites its scale in LDS after the wave's wait, and another
-      // wave's copy of the same word could still land after that
-      if (SCALE == kScaleToken && lane < 16)
-        lds_dma4(a.kv_scale + (int64_t)pg * kPage + qw * 16, lane * 4, lds_addr(&s_scale[it % T::NBUF][qw * 16]));
-    };
-    auto dma_load = [&](int j) { lds_dma16(dma_src + 64 * j, goff, dma_dst + j * 1024); };
-    auto prologue = [&]() {
+    // LDS byte offsets of this lane's K chunk 2p + sg (token 32th + sn: quarter
+    // tq, token tm of it) within a V buffer (p < 16, plus (p / 2) KB) and a rope
+    // buffer (p = 16, 17), for even and odd p
+    const int tq = 2 * th + (sn >> 4), tm = sn & 15;
+    uint32_t kvl[2], krl[2];
 #pragma unroll
-      for (int k = 0; k < T::DIST; ++k)
-        if (k < n_it) {
-          dma_page(k);
-#pragma unroll
-          for (int j = 0; j < T::LOADS; ++j) dma_load(j);
-        }
-    };
-    prologue();
-
-    // Query operands LDS -> VGPRs: lane (m, g) holds rows rb*16 + m and, for
-    // k-block kb, dims 64(kb/2) + 16g + 8(kb%2) .. +8; k-blocks 2i and 2i+1
-    // take the 16 consecutive dims of one 16-byte FP8 chunk of K.
-    if (n_it >= 2)
-      wait_vmcnt<2 * LPP>();
-    else
-      wait_vmcnt<LPP>();
-    __syncthreads();  // (1) every score wave's share of the query is in LDS
-    bf16x8 qop[2][kD / 32];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int row = rb * 16 + m;
-#pragma unroll
-      for (int kb = 0; kb < kD / 32; ++kb) {
-        const int c = 8 * (kb >> 1) + 2 * g + (kb & 1);
-        qop[rb][kb] = *reinterpret_cast<const bf16x8*>(&s_kv[QBUF][(row * 72 + (c ^ ((row >> 1) & 7))) * 16]);
-      }
+    for (int e = 0; e < 2; ++e) {
+      const int x = (4 * tm + ((2 * e + sg) ^ swz(tm >> 2, tq))) * 16;
+      kvl[e] = (uint32_t)(tq * 8192 + x);
+      krl[e] = (uint32_t)(tq * 1024 + x);
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the query buffer may be overwritten
-
-    float m0[2] = {-INFINITY, -INFINITY};   // log2-domain reference of this lane's rows
-    float ymax[2] = {-INFINITY, -INFINITY};  // running max of score - reference
-    float lsum[2] = {0.0f, 0.0f};           // this lane's share of the softmax sums (fp32 P)
-    float lnrm[2] = {0.0f, 0.0f};           // the same over the bf16-rounded P that PV uses
-    const int tok = qw * 16 + m;            // this lane's token in QK^T
-    const uint32_t klane = (uint32_t)(pslot(tok, g) * 16);  // chunk 4i + g at + 1024 i
-    constexpr int KB = kD / 32;
-    u32x4 kraw[KB / 2];  // this wave's K bytes of the next page, read ahead
-
-    // Rows appended in this launch that fall among this wave's 16 tokens of
-    // page it: the wave encodes each one exactly as kv_append_fp8 does and
-    // puts it over the row the copy brought (the cache still held the old
-    // contents); row group 0 also writes it, and its per-token scale, to the
-    // cache for later steps (unless the caller stores the rows itself).  Both row groups compute the same bytes, so it
-    // does not matter which copy the other group's page read saw.
-    auto patch_new_rows = [&](int it, uint8_t* kv) {
-      const int t_first = (p_begin + it) * kPage + qw * 16;
-      const int first_new = L - a.n_new;
-      const int lo = max(first_new, t_first), hi = min(L, t_first + 16);
-      for (int pos = lo; pos < hi; ++pos) {
-        u32x2 codes[2];
-        const float sc = encode_row_e4m3<SCALE == kScaleToken>(
-            a.kv_new + ((int64_t)b * a.n_new + (pos - first_new)) * kD, lane, tscale, codes);
-        const int t = pos & (kPage - 1);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int c8 = lane + 64 * c;  // 8-byte chunk of the row
-          if (c == 0 || lane < 8)
-            *reinterpret_cast<u32x2*>(kv + pslot(t, c8 >> 1) * 16 + 8 * (c8 & 1)) = codes[c];
-        }
-        if (SCALE == kScaleToken && lane == 0) s_scale[it % T::NBUF][t] = sc;
-        bool store = rg == 0 && a.store_rows;
-        if (CHECKED && store) {
-          // the page check runs beside this launch: store only into a page
-          // that is in the pool, is the recorded one and carries its tag
-          const int64_t e = bt_row + pos / kPage;
-          const int raw = load_const(a.block_table, e);
-          const uint32_t cur = load_const(a.page_tags, min(max(raw, 0), a.num_pages - 1));
-          store = raw >= 0 && raw < a.num_pages && raw == load_const(a.expected_pages, e) &&
-                  cur == load_const(a.expected_tags, e);
-        }
-        if (store) {
-          const int pg = min(max(load_const(a.block_table, bt_row + pos / kPage), 0), a.num_pages - 1);
-          uint8_t* dst = a.cache_out + ((int64_t)pg * kPage + t) * kD;
-          *reinterpret_cast<u32x2*>(dst + 8 * lane) = codes[0];
-          if (lane < 8) *reinterpret_cast<u32x2*>(dst + 8 * (lane + 64)) = codes[1];
-          if (SCALE == kScaleToken && lane == 0) a.scale_out[(int64_t)pg * kPage + t] = sc;
-        }
-      }
-      // the row loads and stores are counted like the copies: let them all
-      // finish so the later waits keep their meaning
-      if (lo < hi) wait_vmcnt<0>();
+    float m0 = -INFINITY;    // log2-domain reference of this lane's row
+    float ymax = -INFINITY;  // running max of score - reference
+    float lsum = 0.0f;       // this lane's share of the softmax sum (fp32 P)
+    float lnrm = 0.0f;       // the same over the bf16-rounded P that P V uses
+    constexpr int KP = kD / 32;  // 18 16-byte chunks per token and k half
+    constexpr int KW = 9;        // K chunks held in registers at a time
+    u32x4 kraw[KW];              // chunk p of the page in kraw[p % KW]
+    auto k_read = [&](int it, int p) {
+      kraw[p % KW] = p < 16 ? *reinterpret_cast<const u32x4*>(s_v + (it % kVBuf) * kVBytes + kvl[p & 1] + (p >> 1) * 1024)
+                            : *reinterpret_cast<const u32x4*>(s_rope + (it % kRBuf) * kRBytes + krl[p & 1]);
     };
-
-    // Wait for this wave's own share of page it, zero its rows past the end of
-    // the request (they may hold anything, even NaN codes, and P V multiplies
-    // them by zero weights), and read its K bytes.  Loads complete in order, so
-    // the wait allows exactly the loads issued after page it's: the whole next
-    // page (LPP) when one is in flight behind it, none at the end of the split.
-    auto k_read = [&](int it, bool page_behind) {
-      if (page_behind)
-        wait_vmcnt<LPP>();
-      else
-        wait_vmcnt<0>();
-      uint8_t* kv = s_kv[it % T::NBUF];
-      const int nvalid = L - (p_begin + it) * kPage;
-      if (nvalid < qw * 16 + 16) {
-        // tokens tl0 .. 15 of this wave's quarter: slots tl0 * 4 .. 63 of each group
-        const int tl0 = max(nvalid - qw * 16, 0);
-        const int per = (16 - tl0) * 4;
-        u32x4* q = reinterpret_cast<u32x4*>(kv) + qw * 576 + tl0 * 4;
-        for (int e = lane; e < 9 * per; e += 64) {
-          const int grp = e / per;
-          q[grp * 64 + (e - grp * per)] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-      if (a.n_new > 0) patch_new_rows(it, kv);
+    f32x16 S;  // S^T tile: element r is token 32th + 8(r/4) + 4sg + r%4 of the lane's row
+    // QK^T of page it: chunk p feeds k-blocks 2p (even accumulator) and 2p + 1
+    // (odd); each chunk's conversions ride between MFMAs, and once a chunk is
+    // converted its register is refilled with chunk p + 9.  hook(p) runs at
+    // the end of step p.
+    auto qk = [&](int it, auto hook) {
 #pragma unroll
-      for (int i = 0; i < KB / 2; ++i) kraw[i] = *reinterpret_cast<const u32x4*>(kv + klane + 1024 * i);
-    };
-    // S^T[token][row] = K Q^T for this wave's 16 tokens, all 32 rows: one MFMA
-    // pair per k-block with the conversions of the next k-block between them.
-    static_assert(T::LOADS * 2 == kD / 32, "one page load per two k-blocks");
-    auto qk = [&](f32x4 (&S)[2], auto dma_c) {
-      constexpr bool dma = decltype(dma_c)::value;
-      auto lo_word = [&](int kb) { const u32x4 w = kraw[kb >> 1]; return (kb & 1) ? w[2] : w[0]; };
-      auto hi_word = [&](int kb) { const u32x4 w = kraw[kb >> 1]; return (kb & 1) ? w[3] : w[1]; };
-      uint32_t d[2][4];
-      d[0][0] = cvt_e4m3_lo(lo_word(0));
-      d[0][1] = cvt_e4m3_hi(lo_word(0));
-      d[0][2] = cvt_e4m3_lo(hi_word(0));
-      d[0][3] = cvt_e4m3_hi(hi_word(0));
+      for (int p = 0; p < KW; ++p) k_read(it, p);
+      f32x16 se, so;
+      // operands of step p are converted during step p - 1, so no MFMA waits
+      // for the conversions just before it
+      uint32_t E[2][4], O[2][4];
+      auto cvt_even = [&](uint32_t (&d)[4], const u32x4 w) {
+        d[0] = cvt_e4m3_lo(w[0]);
+        d[1] = cvt_e4m3_hi(w[0]);
+        d[2] = cvt_e4m3_lo(w[1]);
+        d[3] = cvt_e4m3_hi(w[1]);
+      };
+      auto cvt_odd = [&](uint32_t (&d)[4], const u32x4 w) {
+        d[0] = cvt_e4m3_lo(w[2]);
+        d[1] = cvt_e4m3_hi(w[2]);
+        d[2] = cvt_e4m3_lo(w[3]);
+        d[3] = cvt_e4m3_hi(w[3]);
+      };
+      cvt_even(E[0], kraw[0]);
+      cvt_odd(O[0], kraw[0]);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 kop = bf16x8_of(d[kb & 1]);
-        uint32_t (&nx)[4] = d[(kb + 1) & 1];
-        if (kb == 0) mfma_vvv0_w(S[0], kop, qop[0][0]); else mfma_vvv_w(S[0], kop, qop[0][kb]);
-        if constexpr (dma) {
-          if ((kb & 1) == 0) dma_load(kb >> 1);
-        }
-        if (kb + 1 < KB) {
-          nx[0] = cvt_e4m3_lo(lo_word(kb + 1));
-          nx[1] = cvt_e4m3_hi(lo_word(kb + 1));
-        }
-        if (kb == 0) mfma_vvv0(S[1], kop, qop[1][0]); else mfma_vvv(S[1], kop, qop[1][kb]);
-        if (kb + 1 < KB) {
-          nx[2] = cvt_e4m3_lo(hi_word(kb + 1));
-          nx[3] = cvt_e4m3_hi(hi_word(kb + 1));
-        }
+      for (int p = 0; p < KP; ++p) {
+        const bool more = p + 1 < KP;
+        if (p == 0) mfma32_first_w(se, bf16x8_of(E[0]), qop[0]); else mfma32(se, bf16x8_of(E[p & 1]), qop[2 * p]);
+        if (more) cvt_even(E[(p + 1) & 1], kraw[(p + 1) % KW]);
+        if (p == 0) mfma32_first(so, bf16x8_of(O[0]), qop[1]); else mfma32(so, bf16x8_of(O[p & 1]), qop[2 * p + 1]);
+        if (more) cvt_odd(O[(p + 1) & 1], kraw[(p + 1) % KW]);
+        if (p + KW < KP) k_read(it, p + KW);
+        hook(p);
       }
-      mfma_drain_s(S[0], S[1], bf16x8_of(d[(KB - 1) & 1]));
+      mfma32_drain(se, so, bf16x8_of(O[(KP - 1) & 1]));
+      S = se + so;
     };
+    auto no_hook = [](int) {};
     // softmax, part 1: y = score * coef - reference (log2 units), masked past
-    // each row's causal limit, and the running maxima.  Lane holds tokens
-    // 16w + 4g + i of rows rb*16 + m.
-    float y[2][4];
-    f32x4 sc = {1.0f, 1.0f, 1.0f, 1.0f};
-    auto scores = [&](const f32x4 (&S)[2], int it) {
-      const int tbase = (p_begin + it) * kPage;
-      float cs[4];
-      if (SCALE == kScaleToken) {
-        sc = *reinterpret_cast<const f32x4*>(&s_scale[it % T::NBUF][qw * 16 + 4 * g]);
+    // the row's causal limit, and the running maximum; S is overwritten with y
+    f32x4 sc[4] = {{1.f, 1.f, 1.f, 1.f}, {1.f, 1.f, 1.f, 1.f}, {1.f, 1.f, 1.f, 1.f}, {1.f, 1.f, 1.f, 1.f}};
+    auto scores = [&](int it) {
+      const int tbase = (p_begin + it) * kPage + 32 * th + 4 * sg;
+      const float mr = m0 == -INFINITY ? 0.0f : m0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cs[i] = coef * sc[i];
-      }
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const float mr = m0[rb] == -INFINITY ? 0.0f : m0[rb];
+      for (int jr = 0; jr < 4; ++jr) {
+        if (SCALE == kScaleToken)
+          sc[jr] = *reinterpret_cast<const f32x4*>(&s_scale[(it % kVBuf) * 64 + 32 * th + 8 * jr + 4 * sg]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          y[rb][i] = __builtin_fmaf(S[rb][i], SCALE == kScaleToken ? cs[i] : coef, -mr);
+          S[4 * jr + i] = __builtin_fmaf(S[4 * jr + i], SCALE == kScaleToken ? coef * sc[jr][i] : coef, -mr);
       }
-      if (tbase + kPage > lim_lo) {
+      if ((p_begin + it) * kPage + kPage > lim_lo) {
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (tbase + qw * 16 + 4 * g + i >= lim[rb]) y[rb][i] = -INFINITY;
+        for (int r = 0; r < 16; ++r)
+          if (tbase + 8 * (r >> 2) + (r & 3) >= lim) S[r] = -INFINITY;
       }
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-        ymax[rb] = max3f(max3f(ymax[rb], y[rb][0], y[rb][1]), y[rb][2], y[rb][3]);
+      for (int r = 0; r < 16; r += 2) ymax = max3f(ymax, S[r], S[r + 1]);
     };
-    // softmax, part 2: weights 2^y as bf16 P into LDS, the sums, and the flag
-    // that asks for a restart when a weight would exceed 2^64
+    // softmax, part 2: weights 2^y as bf16 P into LDS (two 16-byte chunks per
+    // lane: elements 8h .. 8h+7 are tokens 16h + 4sg + i and 16h + 8 + 4sg + i,
+    // the k order P V reads them in), and the sums
     auto weights = [&](int it) {
+      uint8_t* prow = s_p + (it & 1) * kPBytes + lr * 128;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        float e[4];
+      for (int h = 0; h < 2; ++h) {
+        float e[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) e[i] = __builtin_amdgcn_exp2f(y[rb][i]);
-        uint32_t pk[2];
+        for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(S[8 * h + i]);
+        uint32_t pk[4];
         if (SCALE == kScaleToken) {
           // the per-token V scale rides on the weight; the sums stay unscaled
 #pragma unroll
-          for (int i = 0; i < 2; ++i) pk[i] = pack_bf16x2(e[2 * i] * sc[2 * i], e[2 * i + 1] * sc[2 * i + 1]);
+          for (int i = 0; i < 4; ++i)
+            pk[i] = pack_bf16x2(e[2 * i] * sc[2 * h + (i >> 1)][(2 * i) & 3], e[2 * i + 1] * sc[2 * h + (i >> 1)][(2 * i + 1) & 3]);
         } else {
 #pragma unroll
-          for (int i = 0; i < 2; ++i) pk[i] = pack_bf16x2(e[2 * i], e[2 * i + 1]);
-          lnrm[rb] = dot2_bf16_ones(pk[1], dot2_bf16_ones(pk[0], lnrm[rb]));
+          for (int i = 0; i < 4; ++i) {
+            pk[i] = pack_bf16x2(e[2 * i], e[2 * i + 1]);
+            lnrm = dot2_bf16_ones(pk[i], lnrm);
+          }
         }
-        lsum[rb] += (e[0] + e[1]) + (e[2] + e[3]);
-        *reinterpret_cast<u32x2*>(s_p[it & 1] + (rb * 16 + m) * T::PSTRIDE + (qw * 16 + 4 * g) * 2) =
-            u32x2{pk[0], pk[1]};
+        lsum += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        // 16-byte chunk 4th + 2h + sg of the row, swizzled by the row
+        *reinterpret_cast<u32x4*>(prow + (((4 * th + 2 * h + sg) ^ ((lr >> 1) & 7)) << 4)) =
+            u32x4{pk[0], pk[1], pk[2], pk[3]};
       }
-      const bool over = ymax[0] > kRefSlack || ymax[1] > kRefSlack;
+    };
+    auto set_flag = [&](int it, bool over) {
       const bool any_over = __any(over);
-      if (lane == 0) s_flag[it & 1][qw] = any_over ? 1 : 0;
+      if (lane == 0) s_flag[4 * (it & 1) + wave] = any_over ? 1 : 0;
+    };
+    // maximum / sum of the two k-half lanes of a row (lanes l and l ^ 32)
+    auto pair_max = [](float v) {
+      const auto b = __builtin_amdgcn_permlane32_swap(bits_of(v), bits_of(v), false, false);
+      return fmaxf(float_of(b[0]), float_of(b[1]));
+    };
+    auto pair_sum = [](float v) {
+      const auto b = __builtin_amdgcn_permlane32_swap(bits_of(v), bits_of(v), false, false);
+      return float_of(b[0]) + float_of(b[1]);
     };
 
     for (;;) {
-      k_read(0, n_it > 1);
-      {
-        // page 0 (the first page of an attempt)
-        const bool next = T::DIST < n_it;
-        f32x4 S[2];
-        if (next) {
-          dma_page(T::DIST);
-          qk(S, std::true_type{});
-        } else {
-          qk(S, std::false_type{});
-        }
-        if (1 < n_it) k_read(1, next);
-        scores(S, 0);
-        if (!have_ref) {
-          // the reference of each row is its maximum over the first page
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            const float pm = group4_max(ymax[rb]);
-            if (g == 0) s_red[qw][rb * 16 + m] = pm;
-          }
-          __syncthreads();  // (2) first-page maxima in LDS
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            const int row = rb * 16 + m;
-            m0[rb] = fmaxf(fmaxf(s_red[0][row], s_red[1][row]), fmaxf(s_red[2][row], s_red[3][row]));
-            const float mr = m0[rb] == -INFINITY ? 0.0f : m0[rb];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) y[rb][i] -= mr;
-            ymax[rb] -= mr;
-          }
-          have_ref = true;
-        }
-        weights(0);
-      }
-      __syncthreads();  // (3) P and flags of page 0 are in LDS
-      // Page it's flags are read after the barrier that ends it but looked at
-      // only after the next page's QK^T MFMAs have been issued, so that the
-      // LDS latency of the read stays off the page's critical path.  On a
-      // restart that work (and a copy already issued) is simply dropped; the
-      // output waves leave their loop after the same barrier.
-      uint32_t fw = flag_words(0);
-      bool again = false;
-      auto page = [&](int it, auto dma_c) {  // false: leave for a restart
-        constexpr bool dma = decltype(dma_c)::value;
-        if constexpr (dma) dma_page(it + T::DIST);
-        f32x4 S[2];
-        qk(S, dma_c);
-        settle(fw);
-        if (restart_asked(fw)) return false;
-        if (it + 1 < n_it) k_read(it + 1, dma);
-        scores(S, it);
-        weights(it);
-        __syncthreads();  // (4) P and flags of page it are in LDS; page it - 1 is consumed
-        fw = flag_words(it);
-        return true;
-      };
-      int it = 1;
-      bool ok = true;
-      for (; ok && it + T::DIST < n_it; ++it) ok = page(it, std::true_type{});
-      for (; ok && it < n_it; ++it) ok = page(it, std::false_type{});
-      if (ok) settle(fw);
-      again = !ok || restart_asked(fw);
-      if (!again) break;
-      // A weight would exceed 2^64: restart the split with a reference raised
-      // to each row's running maximum.
-      ++restarts;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const float pm = group4_max(ymax[rb]);
-        if (g == 0) s_red[qw][rb * 16 + m] = pm;
-      }
-      wait_vmcnt<0>();
-      __syncthreads();  // (5) every copy landed, the maxima are in LDS
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int row = rb * 16 + m;
-        const float pm = fmaxf(fmaxf(s_red[0][row], s_red[1][row]), fmaxf(s_red[2][row], s_red[3][row]));
-        const float mr = m0[rb] == -INFINITY ? 0.0f : m0[rb];
-        if (pm > -INFINITY) m0[rb] = fmaxf(m0[rb], mr + pm);
-        ymax[rb] = -INFINITY;
-        lsum[rb] = 0.0f;
-        lnrm[rb] = 0.0f;
-      }
-      reload_ids(0);
-      prologue();
-    }
-    // the sums of this wave's tokens for the output waves
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const float ls = group4_sum(lsum[rb]);
-      const float ln = SCALE == kScaleToken ? ls : group4_sum(lnrm[rb]);
-      const int row = rb * 16 + m;
-      if (g == 0) {
-        s_lsum[qw][row] = ls;
-        s_lnrm[qw][row] = ln;
-        if (qw == 0) s_m0[row] = m0[rb];
-      }
-    }
-    __syncthreads();  // (6) sums in LDS
-  } else {
-    // =====================================================================
-    // output waves: the same barrier sequence, P V one page behind
-    // =====================================================================
-    f32x4 O[2][8];  // rows rb*16 + 4g + i, dims 128*qw + 16db + m (VGPRs)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) O[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mfma_zero_o(O);
-    // per-lane LDS offsets of the V reads: lane 2j+h of a 16-lane group
-    // addresses token 8g+j (+32 kt) of its wave's dims; dims 128w + 64(db/4) +
-    // 16(db%4) are chunk 8w + 4(db/4) + db%4, at pslot + 1024 (db/4) + 18432 kt
-    uint32_t voff[4];
-    {
-      const int t = g * 8 + (m >> 1);
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) voff[bb] = (uint32_t)(pslot(t, 8 * qw + bb) * 16 + 8 * (m & 1));
-    }
-    bf16x8 pv_p[2][2];  // [32-token half][row block]
-    u32x2 pv_v[2][8];   // [32-token half][16-dim block]
-    auto pv = [&](int it) {
-      const uint8_t* kvp = s_kv[it % T::NBUF];
-      const uint8_t* pp = s_p[it & 1];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int tok0 = kt * 32 + g * 8;
-#pragma unroll
-        for (int rbp = 0; rbp < 2; ++rbp)
-          pv_p[kt][rbp] = *reinterpret_cast<const bf16x8*>(pp + (rbp * 16 + m) * T::PSTRIDE + tok0 * 2);
-#pragma unroll
-        for (int db = 0; db < 8; ++db)
-          pv_v[kt][db] = lds_read_tr8(kvp + voff[db & 3] + kt * 32 * T::ROW_BYTES + 1024 * (db >> 2));
-      }
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        uint32_t d[2][4];
-        d[0][0] = cvt_e4m3_lo(pv_v[kt][0].x);
-        d[0][1] = cvt_e4m3_hi(pv_v[kt][0].x);
-        d[0][2] = cvt_e4m3_lo(pv_v[kt][0].y);
-        d[0][3] = cvt_e4m3_hi(pv_v[kt][0].y);
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          const bf16x8 vop = bf16x8_of(d[db & 1]);
-          uint32_t (&nx)[4] = d[(db + 1) & 1];
-          mfma_vvv_w(O[0][db], pv_p[kt][0], vop);
-          if (db + 1 < 8) {
-            nx[0] = cvt_e4m3_lo(pv_v[kt][db + 1].x);
-            nx[1] = cvt_e4m3_hi(pv_v[kt][db + 1].x);
-          }
-          mfma_vvv(O[1][db], pv_p[kt][1], vop);
-          if (db + 1 < 8) {
-            nx[2] = cvt_e4m3_lo(pv_v[kt][db + 1].y);
-            nx[3] = cvt_e4m3_hi(pv_v[kt][db + 1].y);
-          }
-        }
-        mfma_drain_o(O, pv_p[kt][0], pv_p[kt][1], bf16x8_of(d[1]));
-      }
-    };
-
-    __syncthreads();  // (1)
-    for (;;) {
+      bool scan = false;
+      __syncthreads();  // (A) page 0 is staged
+      qk(0, no_hook);
+      scores(0);
       if (!have_ref) {
-        __syncthreads();  // (2)
+        // the reference of each row is its maximum over the first page
+        const float pm = pair_max(ymax);
+        if (sg == 0) s_red[th * 64 + lr] = pm;
+        __syncthreads();  // (B) first-page maxima in LDS
+        m0 = fmaxf(s_red[lr], s_red[64 + lr]);
+        const float mr = m0 == -INFINITY ? 0.0f : m0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[r] -= mr;
+        ymax -= mr;
         have_ref = true;
       }
-      __syncthreads();  // (3)
-      // Page it - 1's flags are looked at after P V of page it - 1 has been
-      // issued; when they ask for a restart that P V is wasted work (its
-      // operands are valid) and O is cleared below.
-      uint32_t fo = flag_words(0);
-      bool again = false;
+      weights(0);
+      set_flag(0, ymax > kRefSlack);
+      __syncthreads();  // (C) P and flags of page 0 are in LDS
+      uint32_t fw = flag_word(0);
       for (int it = 1; it < n_it; ++it) {
-        pv(it - 1);
-        settle(fo);
-        if (restart_asked(fo)) {
-          again = true;
-          break;
-        }
-        __syncthreads();  // (4)
-        fo = flag_words(it);
+        qk(it, [&](int p) {
+          if (p == 3) {  // page it - 1's flags, read after the barrier, are looked at here
+            settle(fw);
+            if (allow_scan && fw != 0u) scan = true;
+          }
+        });
+        scores(it);
+        if (!scan) weights(it);
+        set_flag(it, ymax > kRefSlack);
+        __syncthreads();  // (D) P and flags of page it in LDS; page it - 1 consumed
+        fw = flag_word(it);
       }
-      if (!again) {
-        settle(fo);
-        again = restart_asked(fo);
+      settle(fw);
+      if (allow_scan && fw != 0u) scan = true;
+      if (!scan) break;
+      // A weight would exceed 2^64: every page of the split has been scored
+      // since; run it again with each row's maximum as the reference.
+      {
+        const float pm = pair_max(ymax);
+        if (sg == 0) s_red[th * 64 + lr] = pm;
       }
-      if (!again) {
-        pv(n_it - 1);
-        break;
+      __syncthreads();  // (E) maxima in LDS; every copy has landed
+      {
+        const float pm = fmaxf(s_red[lr], s_red[64 + lr]);
+        const float mr = m0 == -INFINITY ? 0.0f : m0;
+        if (pm > -INFINITY) m0 = fmaxf(m0, mr + pm);
+        ymax = -INFINITY;
+        lsum = 0.0f;
+        lnrm = 0.0f;
       }
-      ++restarts;
-      __syncthreads();  // (5)
-      mfma_zero_o(O);
+      allow_scan = false;
     }
+    // the sums of this wave's tokens for the output waves
+    {
+      const float ls = pair_sum(lsum);
+      const float ln = SCALE == kScaleToken ? ls : pair_sum(lnrm);
+      if (sg == 0) {
+        s_lsum[th * 64 + lr] = ls;
+        s_lnrm[th * 64 + lr] = ln;
+        if (th == 0) s_m0[lr] = m0;
+      }
+    }
+    __syncthreads();  // (F) sums in LDS
+    return;
+  }
 
-    __syncthreads();  // (6) the score waves' sums are in LDS; every page buffer is free
-    // Row normalisation: lane r < 32 of each output wave computes row r's
-    // factor into this wave's slice of s_red (free by now); wave 4 also writes
-    // the row's LSE.  The output is a weighted mean with the bf16 weights P V
-    // used; the LSE uses the fp32 weights.
-    const bool single = a.max_splits == 1;
-    const int64_t prow0 = single ? (int64_t)b * a.R + r0 : ((int64_t)b * a.max_splits + split) * a.R + r0;
-    if (lane < kRows) {
-      const int row = lane;
-      const float lt = s_lsum[0][row] + s_lsum[1][row] + s_lsum[2][row] + s_lsum[3][row];
-      const float ln = s_lnrm[0][row] + s_lnrm[1][row] + s_lnrm[2][row] + s_lnrm[3][row];
-      s_red[qw][row] = ln > 0.0f ? tscale / ln : 0.0f;
-      if (qw == 0 && r0 + row < a.R) {
-        const float mr = s_m0[row] == -INFINITY ? 0.0f : s_m0[row];
-        (single ? a.lse : a.lse_part)[prow0 + row] = lt > 0.0f ? (mr + __log2f(lt)) * kLn2 : -INFINITY;
+  // =======================================================================
+  // output waves: the same barrier sequence, P V one page behind, and the
+  // page copies
+  // =======================================================================
+  const int j = wave - 4;  // dims 128j .. 128j+127; copies quarter j
+  constexpr int LPP = kLoads + (SCALE == kScaleToken ? 1 : 0);  // loads per page per wave
+
+  // Page ids of the split, 64 at a time, one per lane; picked out with
+  // readlane so the copy issue never waits on a scalar load.  Ids past the
+  // split are never used; every used one is clamped to the pool.
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(ids) :: "memory");
+  int id_chunk = 0;
+  auto reload_ids = [&](int chunk) {
+    id_chunk = chunk;
+    const int32_t* src = a.block_table + bt_row + min(p_begin + (chunk << 6) + lane, p_end - 1);
+    asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(ids) : "v"(src) : "memory");
+  };
+  // lane l copies token 16j + l/4, chunk 4i + ((l%4) ^ F) of group i
+  const uint32_t goff = (uint32_t)((16 * j + (lane >> 2)) * 576 + (((lane & 3) ^ swz(lane >> 4, j)) << 4));
+  auto dma_page = [&](int it) {
+    if ((it >> 6) != id_chunk) reload_ids(it >> 6);
+    const int pg = min(max(__builtin_amdgcn_readlane(ids, it & 63), 0), a.num_pages - 1);
+    const uint8_t* src = a.cache + (int64_t)pg * (kPage * kD);
+    const uint32_t vdst = lds_addr(s_v + (it % kVBuf) * kVBytes + j * 8192);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lds_dma16(src + 64 * i, goff, vdst + 1024 * i);
+    lds_dma16(src + 64 * 8, goff, lds_addr(s_rope + (it % kRBuf) * kRBytes + j * 1024));
+    // the scales of this wave's own 16 tokens: a row appended in this launch
+    // overwrites its scale in LDS after this wave's wait
+    if (SCALE == kScaleToken && lane < 16)
+      lds_dma4(a.kv_scale + (int64_t)pg * kPage + 16 * j, lane * 4, lds_addr(&s_scale[(it % kVBuf) * 64 + 16 * j]));
+  };
+
+  // Rows appended in this launch that fall in this wave's quarter of page it:
+  // encoded exactly as kv_append_fp8 does and put over the bytes the copy
+  // brought (the cache still held the old contents); row group 0 also writes
+  // them, and their per-token scales, to the cache for later steps.  Rows go
+  // to positions L_raw - n_new + r; a row past the cache's reach is skipped.
+  auto patch_new_rows = [&](int it) {
+    const int t_first = (p_begin + it) * kPage + 16 * j;
+    const int64_t first_new = (int64_t)L_raw - a.n_new;
+    const int lo = (int)max(first_new, (int64_t)t_first), hi = min(L, t_first + 16);
+    for (int pos = lo; pos < hi; ++pos) {
+      u32x2 codes[2];
+      const float sc = encode_row_e4m3<SCALE == kScaleToken>(
+          a.kv_new + ((int64_t)b * a.n_new + (pos - first_new)) * kD, lane, tscale, codes);
+      const int t = pos & (kPage - 1), tm = t & 15;
+      const int f = swz(tm >> 2, j);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int c8 = lane + 64 * c;  // 8-byte chunk of the row
+        if (c == 0 || lane < 8) {
+          const int c16 = c8 >> 1;
+          uint8_t* dst = c16 < 32 ? s_v + (it % kVBuf) * kVBytes + (j * 512 + (c16 >> 2) * 64 + 4 * tm + ((c16 & 3) ^ f)) * 16
+                                  : s_rope + (it % kRBuf) * kRBytes + (j * 64 + 4 * tm + ((c16 & 3) ^ f)) * 16;
+          *reinterpret_cast<u32x2*>(dst + 8 * (c8 & 1)) = codes[c];
+        }
+      }
+      if (SCALE == kScaleToken && lane == 0) s_scale[(it % kVBuf) * 64 + t] = sc;
+      bool store = rg == 0 && a.store_rows;
+      const int64_t e = bt_row + pos / kPage;
+      const int raw = load_const(a.block_table, e);
+      // never write through a page id outside the pool
+      store = store && raw >= 0 && raw < a.num_pages;
+      if (CHECKED && store) {
+        // the page check runs beside this launch: store only for a length
+        // inside the map and into the recorded page carrying its tag
+        const uint32_t cur = load_const(a.page_tags, raw);
+        store = L_raw >= 0 && L_raw <= cap && raw == load_const(a.expected_pages, e) &&
+                cur == load_const(a.expected_tags, e);
+      }
+      if (store) {
+        uint8_t* dst = a.cache_out + ((int64_t)raw * kPage + t) * kD;
+        *reinterpret_cast<u32x2*>(dst + 8 * lane) = codes[0];
+        if (lane < 8) *reinterpret_cast<u32x2*>(dst + 8 * (lane + 64)) = codes[1];
+        if (SCALE == kScaleToken && lane == 0) a.scale_out[(int64_t)raw * kPage + t] = sc;
       }
     }
-    // O goes out through LDS so that each store moves 16 contiguous bytes:
-    // this wave's 32 x 128 fp32 tile, rows 132 floats apart (conflict-free
-    // writes of the MFMA layout), then 8 dims of one row per lane.  Only this
-    // wave touches its tile, and a wave's LDS accesses complete in order.
-    constexpr int SST = 132;
-    float* tile = reinterpret_cast<float*>(&s_kv[0][0]) + qw * (kRows * SST);
+    // the row loads and stores are counted like the copies: let them all
+    // finish so the later waits keep their meaning
+    if (lo < hi) wait_vmcnt<0>();
+  };
+  // This wave's quarter of page it has landed (the caller waited): zero its
+  // tokens past the end of the request (they may hold anything, even NaN
+  // codes, and P V multiplies them by zero weights), then the new rows.
+  auto staged = [&](int it) {
+    const int nvalid = L - (p_begin + it) * kPage;
+    if (nvalid < 16 * j + 16) {
+      const int tl0 = max(nvalid - 16 * j, 0);
+      const int per = (16 - tl0) * 4;  // slots per group
+      u32x4* v = reinterpret_cast<u32x4*>(s_v + (it % kVBuf) * kVBytes) + j * 512 + tl0 * 4;
+      for (int e = lane; e < 8 * per; e += 64) {
+        const int grp = e / per;
+        v[grp * 64 + (e - grp * per)] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (a.n_new > 0) patch_new_rows(it);
+  };
+
+  // O^T = V^T P^T on the matrix core, so that lane (m, g) of [rb][db] holds
+  // dims 128j + 16db + 4g + i (i < 4) of row 16rb + m: four consecutive output
+  // values of one row, stored straight from registers at the end.  Row blocks
+  // 0, 1 in Oa, 2, 3 in Ob (two arrays, each handed whole to the MFMA fences,
+  // so both stay in VGPRs).
+  f32x4 Oa[2][8], Ob[2][8];
+  // Per-lane LDS offsets of the V reads.  Lane 2jj + h of 16-lane group g
+  // addresses the token of k index 8g + jj of the 32-token block kb, bytes
+  // 8h .. 8h+7 of 16-byte chunk 8j + db: token 32kb + 16(g/2) + mm with
+  // mm = 4(g%2) + jj + 4(jj/4), the order the score waves write P in (their
+  // S^T tiles hold tokens 8r' + 4sg + i).  Within quarter 2kb + g/2 that is
+  // slot (2j + db/4)*64 + 4mm + ((db%4) ^ F), F = (mm/4) ^ 2(g/2).
+  uint32_t voff[4];
+  {
+    const int jj = m >> 1, h = m & 1, hq = g >> 1;
+    const int mm = 4 * (g & 1) + jj + 4 * (jj >> 2);
+    const int f = (mm >> 2) ^ (hq << 1);
 #pragma unroll
-    for (int rbp = 0; rbp < 2; ++rbp)
+    for (int d3 = 0; d3 < 4; ++d3) voff[d3] = (uint32_t)((hq * 512 + 4 * mm + (d3 ^ f)) * 16 + 8 * h);
+  }
+  const uint32_t poff = (uint32_t)(m * 128);  // + row block, chunk (kb, g) ^ (m >> 1)
+  auto pv = [&](int it) {
+    const uint8_t* vb = s_v + (it % kVBuf) * kVBytes;
+    const uint8_t* pp = s_p + (it & 1) * kPBytes;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 pop[4];  // [row block]
+      u32x2 vraw[8];  // [16-dim block]
 #pragma unroll
-        for (int db = 0; db < 8; ++db) tile[(rbp * 16 + 4 * g + i) * SST + 16 * db + m] = O[rbp][db][i];
-    uint16_t* dst = (single ? a.out : a.o_part) + prow0 * kDV + qw * 128;
+      for (int rb = 0; rb < 4; ++rb)
+        pop[rb] = *reinterpret_cast<const bf16x8*>(pp + poff + rb * 2048 + (((4 * kb + g) ^ ((m >> 1) & 7)) << 4));
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int row = k * 4 + (lane >> 4), c = lane & 15;  // 32 rows x 16 chunks of 8 dims
-      const f32x4 v0 = *reinterpret_cast<const f32x4*>(&tile[row * SST + 8 * c]);
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(&tile[row * SST + 8 * c + 4]);
-      const float inv = s_red[qw][row];
-      if (r0 + row < a.R)
-        *reinterpret_cast<u32x4*>(dst + (int64_t)row * kDV + 8 * c) =
-            u32x4{pack_bf16x2(v0.x * inv, v0.y * inv), pack_bf16x2(v0.z * inv, v0.w * inv),
-                  pack_bf16x2(v1.x * inv, v1.y * inv), pack_bf16x2(v1.z * inv, v1.w * inv)};
+      for (int db = 0; db < 8; ++db)
+        vraw[db] = lds_read_tr8(vb + voff[db & 3] + kb * 16384 + (2 * j + (db >> 2)) * 1024);
+      uint32_t d[2][4];
+      d[0][0] = cvt_e4m3_lo(vraw[0].x);
+      d[0][1] = cvt_e4m3_hi(vraw[0].x);
+      d[0][2] = cvt_e4m3_lo(vraw[0].y);
+      d[0][3] = cvt_e4m3_hi(vraw[0].y);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const bf16x8 vop = bf16x8_of(d[db & 1]);
+        uint32_t (&nx)[4] = d[(db + 1) & 1];
+        const bool more = db + 1 < 8;
+        mfma_vvv_w(Oa[0][db], vop, pop[0]);
+        if (more) nx[0] = cvt_e4m3_lo(vraw[db + 1].x);
+        mfma_vvv(Oa[1][db], vop, pop[1]);
+        if (more) nx[1] = cvt_e4m3_hi(vraw[db + 1].x);
+        mfma_vvv(Ob[0][db], vop, pop[2]);
+        if (more) nx[2] = cvt_e4m3_lo(vraw[db + 1].y);
+        mfma_vvv(Ob[1][db], vop, pop[3]);
+        if (more) nx[3] = cvt_e4m3_hi(vraw[db + 1].y);
+      }
+      mfma_drain_o(Oa, pop[0], pop[1], bf16x8_of(d[1]));
+      mfma_tie_o(Ob, pop[2], pop[3], bf16x8_of(d[1]));
+      phase_fence();
+    }
+  };
+
+  // pages 0 and 1 go out before the query barrier (their buffers are not the
+  // query's); a rerun sends them again at the end of its first pass
+  auto first_pages = [&]() {
+    dma_page(0);
+    if (n_it > 1) dma_page(1);
+  };
+  first_pages();
+  __syncthreads();  // (Q)
+  for (;;) {
+    bool scan = false;
+    mfma_def_zero_o(Oa);
+    mfma_def_zero_o(Ob);
+    // page 0 landed
+    if (n_it > 1) wait_vmcnt<LPP>(); else wait_vmcnt<0>();
+    staged(0);
+    __syncthreads();  // (A)
+    if (!have_ref) {
+      __syncthreads();  // (B) the score waves have read the query: its buffers are free
+      have_ref = true;
+    }
+    if (n_it > 2) dma_page(2);
+    if (n_it > 1) {
+      if (n_it > 2) wait_vmcnt<LPP>(); else wait_vmcnt<0>();
+      staged(1);
+    }
+    __syncthreads();  // (C)
+    // Page it - 1's flags are looked at after P V of page it - 1 has been
+    // issued; when they ask for a scan that P V is wasted work (its operands
+    // are valid) and O is cleared before the rerun.
+    // (The last page's P V runs in the last pass of the loop, before that
+    // page's flags are looked at; a scan then throws it away with the rest.)
+    uint32_t fo = flag_word(0);
+    for (int it = 1; it <= n_it; ++it) {
+      if (it + 2 < n_it) dma_page(it + 2);
+      phase_fence();
+      if (!scan) pv(it - 1);
+      settle(fo);
+      if (allow_scan && fo != 0u) scan = true;
+      if (it == n_it) break;
+      if (it + 1 < n_it) {
+        if (it + 2 < n_it) wait_vmcnt<LPP>(); else wait_vmcnt<0>();
+        staged(it + 1);
+      }
+      __syncthreads();  // (D)
+      fo = flag_word(it);
+    }
+    if (!scan) break;
+    __syncthreads();  // (E)
+    allow_scan = false;
+    if (id_chunk != 0) reload_ids(0);
+    first_pages();
+  }
+
+  __syncthreads();  // (F) the score waves' sums are in LDS; every page buffer is free
+  // Normalisation: lane (m, g) owns rows 16rb + m; the output is a weighted
+  // mean with the bf16 weights P V used, the LSE uses the fp32 weights (lanes
+  // g == 0 of wave 4 write it).
+  const bool single = a.max_splits == 1;
+  const int64_t prow0 = single ? (int64_t)b * a.R + r0 : ((int64_t)b * a.max_splits + split) * a.R + r0;
+  float inv[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int row = 16 * rb + m;
+    const float ln = s_lnrm[row] + s_lnrm[64 + row];
+    inv[rb] = ln > 0.0f ? tscale / ln : 0.0f;
+    if (j == 0 && g == 0 && r0 + row < a.R) {
+      const float lt = s_lsum[row] + s_lsum[64 + row];
+      const float mr = s_m0[row] == -INFINITY ? 0.0f : s_m0[row];
+      (single ? a.lse : a.lse_part)[prow0 + row] = lt > 0.0f ? (mr + __log2f(lt)) * kLn2 : -INFINITY;
     }
   }
+  // Stores: lane (m, g) holds, per [rb][db], four consecutive bf16 of row
+  // 16rb + m.  They go through LDS (this wave's 64 rows x 256 bytes, rows 272
+  // bytes apart: conflict-free 8-byte writes of this layout and 16-byte reads
+  // of whole rows) so that each store moves 16 contiguous bytes per lane and
+  // 16 lanes fill one row's 256 bytes.  Only this wave touches its tile, and a
+  // wave's LDS accesses complete in order.
+  mfma_result_fence_v16(Oa);
+  mfma_result_fence_v16(Ob);
+  constexpr int kTileStride = 272;
+  uint8_t* tile = lds + j * (kRows8 * kTileStride);
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const f32x4 o = rb < 2 ? Oa[rb][db] : Ob[rb - 2][db];
+      *reinterpret_cast<u32x2*>(tile + (16 * rb + m) * kTileStride + 32 * db + 8 * g) =
+          u32x2{pack_bf16x2(o[0] * inv[rb], o[1] * inv[rb]), pack_bf16x2(o[2] * inv[rb], o[3] * inv[rb])};
+    }
+  uint16_t* dst = (single ? a.out : a.o_part) + prow0 * kDV + j * 128;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int row = 4 * k + (lane >> 4), c = lane & 15;  // 64 rows x 16 chunks of 8 dims
+    const u32x4 v = *reinterpret_cast<const u32x4*>(tile + row * kTileStride + 16 * c);
+    if (r0 + row < a.R) *reinterpret_cast<u32x4*>(dst + (int64_t)row * kDV + 8 * c) = v;
+  }
 }
+
+}  // namespace
+
+int decode_rows_fp8() { return kRows8; }
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, int scale_mode, hipStream_t stream) {
   const bool checked = a.status != nullptr;

@@ -17,7 +17,7 @@ from . import _lib
 class DecodeStep:
     def __init__(self, B, n_q, H, max_blocks, max_seq_len, total_seq_len, device, num_cus=0,
                  pages_per_split=None, max_splits=None, fuse_append=True, seq_lens_host=None,
-                 check_mode="launch"):
+                 check_mode="launch", cache_dtype="fp8"):
         """seq_lens_host: the batch's lengths on the host, when known; the split
         plan is then fitted to them (mla_decode_plan_lens) instead of to the
         longest and the summed length alone.  check_mode, where the page check
@@ -26,14 +26,16 @@ class DecodeStep:
           "launch"  inside the decode launch (mla_decode_paged_append_checked),
                     the combine masking flagged requests (the default);
           "front"   kv_check_pages, then the step on the checked lengths;
-          "stream"  beside the decode on a second stream (see _overlapped)."""
+          "stream"  beside the decode on a second stream (see _overlapped).
+        cache_dtype: "fp8" or "bf16", the cache the plan is made for."""
         self.fuse_append = fuse_append
         if pages_per_split is None or max_splits is None:
             if seq_lens_host is not None:
-                pages_per_split, max_splits = _lib.mla_decode_plan_lens(seq_lens_host, n_q, H, num_cus)
+                pages_per_split, max_splits = _lib.mla_decode_plan_lens(seq_lens_host, n_q, H, num_cus,
+                                                                        cache_dtype)
             else:
                 pages_per_split, max_splits = _lib.mla_decode_plan(B, n_q, H, max_seq_len, total_seq_len,
-                                                                   num_cus)
+                                                                   num_cus, cache_dtype)
         self.B, self.n_q, self.H, self.max_blocks = B, n_q, H, max_blocks
         self.pps, self.max_splits = int(pages_per_split), int(max_splits)
         self.out = torch.empty((B, n_q, H, _lib.VALUE_DIM), dtype=torch.bfloat16, device=device)

@@ -83,7 +83,7 @@ class GpuState:
         w = self.w
         st = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(),
                             self.device, num_cus=num_cus, pages_per_split=pages_per_split,
-                            max_splits=max_splits, seq_lens_host=w.seq_lens)
+                            max_splits=max_splits, seq_lens_host=w.seq_lens, cache_dtype=w.cache_dtype)
         out, lse = st(self.q, self.cache, self.kv_scale, self.scale_mode, self.block_table,
                       self.seq_lens, w.softmax_scale, new_rows=self.new_rows)
         torch.cuda.synchronize()
@@ -95,7 +95,7 @@ class GpuState:
 
         w = self.w
         st = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(),
-                            self.device, pages_per_split=pages_per_split, max_splits=max_splits)
+                            self.device, pages_per_split=pages_per_split, max_splits=max_splits, cache_dtype=w.cache_dtype)
         st.decode(self.q, self.cache, self.kv_scale, self.scale_mode, self.block_table, self.seq_lens,
                   w.softmax_scale)
         st.combine(self.seq_lens)

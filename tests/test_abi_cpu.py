@@ -121,6 +121,11 @@ def test_checked_decode_validation(lib):
     assert call(B=0, tags=None, et=None, st=None) == 0
 
 
+# query rows per decode workgroup: 64 on an FP8 cache, 32 on a BF16 cache
+ROWS = {"fp8": 64, "bf16": 32}
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
 @pytest.mark.parametrize("B,n_q,H,maxL,total,cus", [
     (1, 1, 64, 100_001, 100_001, 256),
     (32, 1, 64, 137_661, 3_269_170, 256),
@@ -130,17 +135,17 @@ def test_checked_decode_validation(lib):
     (3, 2, 16, 1, 3, 80),
     (1, 1, 64, 0, 0, 256),
 ])
-def test_plan_covers_every_page(B, n_q, H, maxL, total, cus):
+def test_plan_covers_every_page(B, n_q, H, maxL, total, cus, dtype):
     import long_context_mla_amd as m
 
-    pps, ms = m.mla_decode_plan(B, n_q, H, maxL, total, cus)
+    pps, ms = m.mla_decode_plan(B, n_q, H, maxL, total, cus, dtype)
     pages = -(-maxL // 64)
     assert pps >= 1 and ms >= 1
     assert pps * ms >= pages
     assert pps * (ms - 1) < max(pages, 1)  # no split past the longest request
     if pages:
-        # about one workgroup (32 query rows, pages_per_split pages) per CU
-        rows_groups = -(-(n_q * H) // 32)
+        # about one workgroup (a group of query rows, pages_per_split pages) per CU
+        rows_groups = -(-(n_q * H) // ROWS[dtype])
         total_pages = -(-total // 64) + B
         assert pps <= max(1, -(-(total_pages * rows_groups) // (cus or 256)))
 
@@ -152,9 +157,11 @@ def test_plan_rejects_bad_input():
         m.mla_decode_plan(1, 0, 64, 10, 10)
     with pytest.raises(m.MlaError):
         m.mla_decode_plan(1, 1, 64, -1, 10)
+    with pytest.raises(m.MlaError):
+        m.mla_decode_plan(1, 1, 64, 10, 10, 0, 7)  # no such cache dtype
 
 
-def _model_makespan(lens, n_q, H, pps, cus, fixed=2):
+def _model_makespan(lens, n_q, H, pps, cus, fixed=2, rows=64):
     """The planner's duration model written out: workgroups in 1-D launch order
     (units b * max_splits + split round robin over 8 XCDs, row groups
     consecutive), workgroup i on the first free compute unit of XCD i % 8,
@@ -163,7 +170,7 @@ def _model_makespan(lens, n_q, H, pps, cus, fixed=2):
 
     pages = [-(-int(L) // 64) for L in lens]
     ms = -(-max(pages) // pps)
-    n_rg = -(-(n_q * H) // 32)
+    n_rg = -(-(n_q * H) // rows)
     B = len(lens)
     grid = (B * ms + 7) // 8 * 8 * n_rg
     pools = [[0] * max(1, cus // 8) for _ in range(8)]
@@ -200,11 +207,12 @@ def _lens(kind):
     return [0, 0]
 
 
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
 @pytest.mark.parametrize("kind,n_q,H,cus", [
     ("single", 1, 64, 256), ("uniform32", 1, 64, 256), ("lognormal64", 1, 64, 256),
     ("spec16", 4, 64, 256), ("tiny", 2, 16, 80), ("empty", 1, 64, 256), ("lognormal64", 1, 64, 7),
 ])
-def test_plan_lens(kind, n_q, H, cus):
+def test_plan_lens(kind, n_q, H, cus, dtype):
     """mla_decode_plan_lens covers every page with at most one short split per
     request, fits its workgroups into at most four rounds when the requests
     allow it, and (under its own duration model) never does worse than the
@@ -212,19 +220,20 @@ def test_plan_lens(kind, n_q, H, cus):
     import long_context_mla_amd as m
 
     lens = _lens(kind)
-    pps, ms = m.mla_decode_plan_lens(lens, n_q, H, cus)
+    pps, ms = m.mla_decode_plan_lens(lens, n_q, H, cus, dtype)
     pages = [-(-int(L) // 64) for L in lens]
     assert pps >= 1 and ms >= 1
     if max(pages) == 0:
         assert (pps, ms) == (1, 1)
         return
     assert pps * ms >= max(pages) and pps * (ms - 1) < max(pages)
-    n_rg = -(-(n_q * H) // 32)
+    n_rg = -(-(n_q * H) // ROWS[dtype])
     wgs = sum(max(1, -(-p // pps)) for p in pages) * n_rg
     if len(lens) * n_rg <= 4 * cus:
         assert wgs <= 4 * cus
-    old = m.mla_decode_plan(len(lens), n_q, H, max(lens), sum(lens), cus)[0]
-    assert _model_makespan(lens, n_q, H, pps, cus) <= _model_makespan(lens, n_q, H, old, cus)
+    old = m.mla_decode_plan(len(lens), n_q, H, max(lens), sum(lens), cus, dtype)[0]
+    rows = ROWS[dtype]
+    assert _model_makespan(lens, n_q, H, pps, cus, rows=rows) <= _model_makespan(lens, n_q, H, old, cus, rows=rows)
 
 
 def test_plan_lens_rejects_bad_input():

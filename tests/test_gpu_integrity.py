@@ -128,7 +128,7 @@ def _e2e_step(w, g, tags, et, fuse_append, check_mode, stream=None):
     npg = int(-(-w.seq_lens.max() // 64))
     st = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(), g.device,
                         pages_per_split=2, max_splits=-(-npg // 2), fuse_append=fuse_append,
-                        check_mode=check_mode)
+                        check_mode=check_mode, cache_dtype=w.cache_dtype)
     check = (_dev(tags), _dev(et), None)
     return st, check
 
@@ -261,7 +261,7 @@ def test_in_launch_check_with_an_earlier_stale_page():
     # the victim's new row went to its own last page, as a check-free append puts it
     ref = GpuState(w)
     ref_st = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(), ref.device,
-                            pages_per_split=st.pps, max_splits=st.max_splits)
+                            pages_per_split=st.pps, max_splits=st.max_splits, cache_dtype=w.cache_dtype)
     ref_st(ref.q, ref.cache, ref.kv_scale, ref.scale_mode, ref.block_table, ref.seq_lens, w.softmax_scale,
            new_rows=ref.new_rows)
     torch.cuda.synchronize()
@@ -303,7 +303,7 @@ def test_in_launch_status_matches_oracle():
     g.seq_lens = _dev(lens)
     npg = int(-(-w.seq_lens.max() // 64))
     st = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(), g.device,
-                        pages_per_split=16, max_splits=-(-npg // 16), check_mode="launch")
+                        pages_per_split=16, max_splits=-(-npg // 16), check_mode="launch", cache_dtype=w.cache_dtype)
     out, lse = st(g.q, g.cache, g.kv_scale, g.scale_mode, g.block_table, g.seq_lens, w.softmax_scale,
                   new_rows=g.new_rows, page_check=(_dev(tags), _dev(et), _dev(ep)))
     torch.cuda.synchronize()

@@ -131,7 +131,7 @@ def test_fused_append_equals_separate(mode):
         for fuse in (False, True):
             g = GpuState(w)
             st = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(),
-                                g.device, pages_per_split=pps, max_splits=ms, fuse_append=fuse)
+                                g.device, pages_per_split=pps, max_splits=ms, fuse_append=fuse, cache_dtype=w.cache_dtype)
             o, l = st(g.q, g.cache, g.kv_scale, g.scale_mode, g.block_table, g.seq_lens, w.softmax_scale,
                       new_rows=g.new_rows)
             torch.cuda.synchronize()
@@ -193,7 +193,7 @@ def test_constant_column_gives_exactly_one():
 def _plan(w):
     import long_context_mla_amd as mla
 
-    return mla.mla_decode_plan(w.B, w.n_q, w.H, int(w.seq_lens.max()), w.total_tokens())
+    return mla.mla_decode_plan(w.B, w.n_q, w.H, int(w.seq_lens.max()), w.total_tokens(), cache_dtype=w.cache_dtype)
 
 
 def test_page_permutation_and_determinism_bitwise():
@@ -220,7 +220,11 @@ def test_page_permutation_and_determinism_bitwise():
 
 def test_fp8_equals_bf16_on_the_e4m3_grid():
     """Cache values exactly representable in e4m3 with scale 1: the FP8 path and
-    the BF16 path see identical numbers and must agree bit for bit."""
+    the BF16 path see identical numbers.  The two kernels feed the tokens to the
+    matrix core in different orders (64 and 32 query rows per workgroup, other
+    k orders), so fp32 rounding may differ; a wrong decode of any code would
+    not stay inside these bounds (the codes span the whole e4m3 range, so the
+    softmax is peaked and each output row is dominated by a few decoded rows)."""
     w8 = synth.custom("grid", B=2, n_q=2, H=64, context_lens=(900, 130), cache_dtype="fp8",
                       scale_mode="tensor", seed=8, append=0)
     g8 = GpuState(w8)
@@ -238,7 +242,12 @@ def test_fp8_equals_bf16_on_the_e4m3_grid():
     plan = _plan(w8)
     o8, l8 = g8.decode_only(*plan)
     ob, lb = gb.decode_only(*plan)
-    assert np.array_equal(o8, ob) and np.array_equal(l8, lb)
+    scale = max(1.0, float(np.abs(ob).max()))
+    err = float(np.abs(o8 - ob).max())
+    lerr = float(np.abs(l8 - lb).max())
+    log(f"fp8 vs bf16 on the e4m3 grid: max |out| diff {err:.3e} (max |out| {scale:.3e}), lse diff {lerr:.3e}")
+    assert err <= 2.0 ** -7 * scale
+    assert lerr <= 1e-5 * max(1.0, float(np.abs(lb).max()))
 
 
 def test_needles_peaked_softmax():
