@@ -42,7 +42,7 @@ class MlaError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m long_context_mla_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python long_context_mla_amd/build.py` "
             "(hipcc, gfx950); there is no other implementation"
         )
     lib = ctypes.CDLL(LIB_PATH)

@@ -1,6 +1,6 @@
 """Build the gfx950 HIP library in-tree: long_context_mla_amd/libmla_decode.so.
 
-``python -m long_context_mla_amd.build`` compiles every source under ``csrc/``
+``python long_context_mla_amd/build.py`` compiles every source under ``csrc/``
 with hipcc for gfx950 only.
 """
 

@@ -24,7 +24,7 @@ PAGE_BYTES = 36864
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m long_context_mla_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python long_context_mla_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     lib.mla_peak_stream_read.argtypes = [P, L, P, I, P]
