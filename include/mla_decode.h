@@ -30,7 +30,8 @@
  *   E4M3 is the OCP E4M3FN encoding (bias 7, no infinities, max 448).
  *
  * Ownership and threading: the caller owns every buffer; the library never
- * allocates, frees or synchronises.  All pointers except the scalar-out
+ * allocates, frees or synchronises (the one buffer it owns, the static
+ * scratch of mla_decode_paged_append_noalloc, is part of its code object).  All pointers except the scalar-out
  * arguments of mla_decode_plan are device pointers.  Work is enqueued on
  * `stream` (a hipStream_t; NULL = the default stream) and the calls return
  * before it runs.  The calls are re-entrant; calls that write the same buffers
@@ -65,8 +66,14 @@ typedef enum {
   MLA_ERR_NULL_PTR = 1,
   MLA_ERR_BAD_SHAPE = 2,
   MLA_ERR_UNSUPPORTED = 3,
-  MLA_ERR_HIP = 4
+  MLA_ERR_HIP = 4,
+  MLA_ERR_SCRATCH_LIMIT = 5
 } mla_status_t;
+
+/* Split-partial rows (B * max_splits * n_q * H) the fixed scratch of
+ * mla_decode_paged_append_noalloc holds: 32 MiB of bf16 partials plus
+ * 128 KiB of fp32 LSEs per GPU. */
+#define MLA_NOALLOC_MAX_PARTIAL_ROWS 32768
 
 /* Per-request result bits of kv_check_pages (0 = the request may read the cache). */
 typedef enum {
@@ -210,6 +217,42 @@ int mla_decode_paged_append_checked(const void* kv_new, int n_new, const void* q
                                     int max_splits, void* o_partial, float* lse_partial,
                                     const uint32_t* page_tags, const int32_t* expected_pages,
                                     const uint32_t* expected_tags, int32_t* status, void* stream);
+
+/*
+ * mla_decode_paged_append_noalloc — mla_decode_paged_append followed by
+ * mla_decode_combine, with the split partials in a scratch array the library
+ * holds, for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The call
+ * makes no allocation of any kind; the caller passes only inputs and outputs.
+ *
+ *   arguments   as in mla_decode_paged_append, without o_partial and
+ *               lse_partial; out bf16 [B, n_q, H, 512] and lse fp32
+ *               [B, n_q, H] are always written (for max_splits == 1 directly
+ *               by the decode launch, else by the merge launched after it on
+ *               the same stream).
+ *
+ * Results are bit-identical to mla_decode_paged_append + mla_decode_combine
+ * with the same pages_per_split / max_splits (the same kernels run).  The
+ * scratch is a file-scope device array of MLA_NOALLOC_MAX_PARTIAL_ROWS partial
+ * rows; each GPU holds its own copy from the first call on that device until
+ * the process ends.  Nothing in it has to start at zero: the merge reads only
+ * the partials the decode launch of the same call has written.  Every call on
+ * one GPU shares that GPU's scratch, so calls that overlap on one GPU (on
+ * different streams, or from different threads without ordering) race and
+ * give wrong results; calls ordered on one stream are safe.  The stream must
+ * belong to the current device.
+ *
+ * Returns MLA_ERR_SCRATCH_LIMIT when max_splits > 1 and
+ * B * max_splits * n_q * H > MLA_NOALLOC_MAX_PARTIAL_ROWS (nothing launched),
+ * MLA_ERR_NULL_PTR for a NULL out / lse with B > 0, MLA_ERR_UNSUPPORTED for a
+ * stream of another device; otherwise as mla_decode_paged_append.
+ */
+int mla_decode_paged_append_noalloc(const void* kv_new, int n_new, const void* q, void* kv_cache,
+                                    float* kv_scale, int scale_mode, const int32_t* block_table,
+                                    const int32_t* seq_lens, int B, int n_q, int H, int max_blocks,
+                                    int num_pages, float softmax_scale, int pages_per_split,
+                                    int max_splits, void* out, float* lse, int store_rows,
+                                    void* stream);
 
 /*
  * mla_decode_combine — merge the split partials of mla_decode_paged

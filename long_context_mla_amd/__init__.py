@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     CACHE_FP8_E4M3,
     LIB_PATH,
     MlaError,
+    NOALLOC_MAX_PARTIAL_ROWS,
     PAGE_BAD_LEN,
     PAGE_OK,
     PAGE_OUT_OF_RANGE,
@@ -23,6 +24,7 @@ from ._lib import (  # noqa: F401
     mla_decode_combine,
     mla_decode_paged,
     mla_decode_paged_append,
+    mla_decode_paged_append_noalloc,
     mla_decode_plan,
     mla_decode_plan_lens,
     status_string,

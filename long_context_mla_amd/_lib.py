@@ -56,17 +56,22 @@ def _load() -> ctypes.CDLL:
     lib.kv_check_pages.argtypes = [P, I, P, P, P, P, I, I, P, P, P]
     lib.mla_decode_paged_append_checked.argtypes = [P, I, P, P, P, I, P, P, I, I, I, I, I, F, I, I, P, P,
                                                     P, P, P, P, P]
+    lib.mla_decode_paged_append_noalloc.argtypes = [P, I, P, P, P, I, P, P, I, I, I, I, I, F, I, I, P, P, I, P]
     lib.mla_status_string.argtypes = [I]
     lib.mla_status_string.restype = ctypes.c_char_p
     for fn in ("kv_append_fp8", "mla_decode_paged", "mla_decode_paged_append", "mla_decode_combine",
-               "mla_decode_plan", "mla_decode_plan_lens", "kv_check_pages", "mla_decode_paged_append_checked"):
+               "mla_decode_plan", "mla_decode_plan_lens", "kv_check_pages", "mla_decode_paged_append_checked",
+               "mla_decode_paged_append_noalloc"):
         getattr(lib, fn).restype = I
     return lib
 
 
 LIB = _load()
 EXPORTS = ("kv_append_fp8", "mla_decode_paged", "mla_decode_paged_append", "mla_decode_paged_append_checked",
-           "mla_decode_combine", "mla_decode_plan", "mla_decode_plan_lens", "kv_check_pages", "mla_status_string")
+           "mla_decode_paged_append_noalloc", "mla_decode_combine", "mla_decode_plan", "mla_decode_plan_lens", "kv_check_pages", "mla_status_string")
+
+NOALLOC_MAX_PARTIAL_ROWS = 32768
+ERR_SCRATCH_LIMIT = 5
 
 PAGE_OK = 0
 PAGE_BAD_LEN = 1
@@ -233,6 +238,45 @@ def mla_decode_paged_append(kv_new, q, kv_cache, kv_scale, scale_mode, block_tab
         float(softmax_scale), int(pages_per_split), int(max_splits),
         _ptr(o_partial) if max_splits > 1 else None, _ptr(lse_partial) if max_splits > 1 else None,
         _ptr(out) if max_splits == 1 else None, _ptr(lse) if max_splits == 1 else None,
+        1 if store_rows else 0, _stream(stream)))
+
+
+def mla_decode_paged_append_noalloc(kv_new, q, kv_cache, kv_scale, scale_mode, block_table, seq_lens,
+                                    softmax_scale, pages_per_split, max_splits, out, lse, stream=None,
+                                    store_rows=True):
+    """mla_decode_paged_append + mla_decode_combine with the split partials in the
+    library's fixed per-GPU scratch (no allocation); out bf16 [B, n_q, H, 512] and
+    lse fp32 [B, n_q, H] are written.  Calls that overlap on one GPU race."""
+    mode = _SCALE_NAMES[scale_mode] if isinstance(scale_mode, str) else int(scale_mode)
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev, 4)
+    _need(kv_new, "kv_new", torch.bfloat16, dev, 3)
+    if _cache_kind(kv_cache) != CACHE_FP8_E4M3 or kv_cache.dim() != 3:
+        raise TypeError("kv_cache must be E4M3 codes [num_pages, 64, 576]")
+    _need(kv_cache, "kv_cache", kv_cache.dtype, dev)
+    _need(kv_scale, "kv_scale", torch.float32, dev)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    _need(out, "out", torch.bfloat16, dev, 4)
+    _need(lse, "lse", torch.float32, dev, 3)
+    B, n_q, H, D = q.shape
+    num_pages = kv_cache.shape[0]
+    if D != HEAD_DIM or tuple(kv_cache.shape[1:]) != (PAGE_SIZE, HEAD_DIM):
+        raise ValueError("row width must be 576 and pages [64, 576]")
+    if kv_new.shape[0] != B or kv_new.shape[2] != HEAD_DIM:
+        raise ValueError("kv_new must be [B, n_new, 576]")
+    if block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("block_table / seq_lens batch mismatch")
+    if mode == SCALE_PER_TOKEN and tuple(kv_scale.shape) != (num_pages, PAGE_SIZE):
+        raise ValueError("per-token kv_scale must be [num_pages, 64]")
+    if mode == SCALE_PER_TENSOR and kv_scale.numel() != 1:
+        raise ValueError("per-tensor kv_scale must have one element")
+    if tuple(out.shape) != (B, n_q, H, VALUE_DIM) or tuple(lse.shape) != (B, n_q, H):
+        raise ValueError("out / lse shape mismatch")
+    _check("mla_decode_paged_append_noalloc", LIB.mla_decode_paged_append_noalloc(
+        _ptr(kv_new), kv_new.shape[1], _ptr(q), _ptr(kv_cache), _ptr(kv_scale), mode,
+        _ptr(block_table), _ptr(seq_lens), B, n_q, H, block_table.shape[1], num_pages,
+        float(softmax_scale), int(pages_per_split), int(max_splits), _ptr(out), _ptr(lse),
         1 if store_rows else 0, _stream(stream)))
 
 

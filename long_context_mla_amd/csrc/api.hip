@@ -1,10 +1,14 @@
 // C-ABI entry points declared in include/mla_decode.h: host-side argument
 // validation (before any HIP call), split planning, and kernel launches on the
-// caller's stream.  No allocation, no synchronisation, no exceptions.
+// caller's stream.  No allocation, no synchronisation, no exceptions.  The one
+// buffer the library owns is the split-partial scratch of
+// mla_decode_paged_append_noalloc below, a static device array.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <functional>
+#include <mutex>
 #include <queue>
 #include <vector>
 
@@ -12,9 +16,65 @@
 #include "device_common.h"
 #include "launch.h"
 
+// Split partials of mla_decode_paged_append_noalloc: MLA_NOALLOC_MAX_PARTIAL_ROWS
+// rows of 512 bf16 (o), then as many fp32 (lse), in the [B, max_splits, R]
+// order of mla_decode_paged's partial buffers.  Every GPU the library runs on
+// holds its own copy until the process ends.  Host code never uses this name
+// as an address: scratch_partials() resolves each device's copy.
+constexpr size_t kScratchOBytes = (size_t)MLA_NOALLOC_MAX_PARTIAL_ROWS * MLA_VALUE_DIM * 2;
+constexpr size_t kScratchBytes = kScratchOBytes + (size_t)MLA_NOALLOC_MAX_PARTIAL_ROWS * 4;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
 
 constexpr int64_t kMaxGrid = 2147483647;
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// The device address of the current device's scratch, looked up once per
+// device; the stream must belong to that device.
+int scratch_partials(hipStream_t stream, void** o_partial, float** lse_partial) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return MLA_ERR_UNSUPPORTED;
+  if (stream) {
+    hipDevice_t sdev = 0;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return MLA_ERR_HIP;
+    if (sdev != dev) return MLA_ERR_UNSUPPORTED;
+  }
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_ERR_HIP;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *o_partial = p;
+  *lse_partial = reinterpret_cast<float*>(static_cast<uint8_t*>(p) + kScratchOBytes);
+  return MLA_OK;
+}
+
+hipError_t combine_launch(const void* o_partial, const float* lse_partial, const int32_t* seq_lens,
+                          int B, int R, int max_blocks, int pps, int max_splits, void* out, float* lse,
+                          const int32_t* status, hipStream_t stream) {
+  mla::CombineArgs a;
+  a.o_part = static_cast<const uint16_t*>(o_partial);
+  a.lse_part = lse_partial;
+  a.seq_lens = seq_lens;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.status = status;
+  a.B = B;
+  a.R = R;
+  a.max_blocks = max_blocks;
+  a.pps = pps;
+  a.max_splits = max_splits;
+  return mla::launch_combine(a, stream);
+}
 
 bool bad_stream_free_shape(int B, int n_q, int H) {
   return B < 0 || B > 65535 || n_q < 1 || n_q > MLA_MAX_QUERIES || H < 1 || H > MLA_MAX_HEADS;
@@ -35,7 +95,8 @@ int decode_impl(const void* q, const void* kv_cache, int cache_dtype, const floa
                 int max_splits, void* o_partial, float* lse_partial, void* out, float* lse,
                 const void* kv_new, int n_new, int store_rows, void* stream,
                 const uint32_t* page_tags = nullptr, const int32_t* expected_pages = nullptr,
-                const uint32_t* expected_tags = nullptr, int32_t* status = nullptr) {
+                const uint32_t* expected_tags = nullptr, int32_t* status = nullptr,
+                bool use_scratch = false) {
   if (int s = check_cache_mode(cache_dtype, scale_mode)) return s;
   if (bad_stream_free_shape(B, n_q, H)) return MLA_ERR_BAD_SHAPE;
   if (max_blocks < 1 || num_pages < 1 || pages_per_split < 1 || max_splits < 1) return MLA_ERR_BAD_SHAPE;
@@ -51,7 +112,16 @@ int decode_impl(const void* q, const void* kv_cache, int cache_dtype, const floa
   if (!q || !kv_cache || !block_table || !seq_lens) return MLA_ERR_NULL_PTR;
   if (scale_mode != MLA_SCALE_NONE && !kv_scale) return MLA_ERR_NULL_PTR;
   if (max_splits == 1 && (!out || !lse)) return MLA_ERR_NULL_PTR;
-  if (max_splits > 1 && (!o_partial || !lse_partial)) return MLA_ERR_NULL_PTR;
+  if (use_scratch) {
+    // partials in the library's scratch, merged into out / lse in this call
+    if (!out || !lse) return MLA_ERR_NULL_PTR;
+    if (max_splits > 1) {
+      if ((int64_t)B * max_splits * R > MLA_NOALLOC_MAX_PARTIAL_ROWS) return MLA_ERR_SCRATCH_LIMIT;
+      if (int s = scratch_partials(static_cast<hipStream_t>(stream), &o_partial, &lse_partial)) return s;
+    }
+  } else if (max_splits > 1 && (!o_partial || !lse_partial)) {
+    return MLA_ERR_NULL_PTR;
+  }
   mla::DecodeArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.cache = static_cast<const uint8_t*>(kv_cache);
@@ -83,7 +153,10 @@ int decode_impl(const void* q, const void* kv_cache, int cache_dtype, const floa
   a.status = status;
   a.check_from = (int)mla::decode_grid_size(B, max_splits, n_rg);
   const int kind = cache_dtype == MLA_CACHE_FP8_E4M3 ? mla::kFp8 : mla::kBf16;
-  const hipError_t e = mla::launch_decode(a, kind, scale_mode, static_cast<hipStream_t>(stream));
+  hipError_t e = mla::launch_decode(a, kind, scale_mode, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && use_scratch && max_splits > 1)
+    e = combine_launch(o_partial, lse_partial, seq_lens, B, R, max_blocks, pages_per_split, max_splits,
+                       out, lse, nullptr, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -98,6 +171,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_BAD_SHAPE: return "bad shape or size argument";
     case MLA_ERR_UNSUPPORTED: return "unsupported configuration";
     case MLA_ERR_HIP: return "HIP launch error";
+    case MLA_ERR_SCRATCH_LIMIT: return "split partials exceed the fixed scratch of the allocation-free call";
     default: return "unknown status";
   }
 }
@@ -191,6 +265,21 @@ int mla_decode_paged_append_checked(const void* kv_new, int n_new, const void* q
                      stream, page_tags, expected_pages, expected_tags, status);
 }
 
+int mla_decode_paged_append_noalloc(const void* kv_new, int n_new, const void* q, void* kv_cache,
+                                    float* kv_scale, int scale_mode, const int32_t* block_table,
+                                    const int32_t* seq_lens, int B, int n_q, int H, int max_blocks,
+                                    int num_pages, float softmax_scale, int pages_per_split,
+                                    int max_splits, void* out, float* lse, int store_rows,
+                                    void* stream) {
+  if (scale_mode != MLA_SCALE_PER_TENSOR && scale_mode != MLA_SCALE_PER_TOKEN) return MLA_ERR_UNSUPPORTED;
+  if (n_new < 0) return MLA_ERR_BAD_SHAPE;
+  if (n_new > 0 && B > 0 && !kv_new) return MLA_ERR_NULL_PTR;
+  return decode_impl(q, kv_cache, MLA_CACHE_FP8_E4M3, kv_scale, scale_mode, block_table, seq_lens, B,
+                     n_q, H, max_blocks, num_pages, softmax_scale, pages_per_split, max_splits, nullptr,
+                     nullptr, out, lse, n_new > 0 ? kv_new : nullptr, n_new, store_rows, stream, nullptr,
+                     nullptr, nullptr, nullptr, true);
+}
+
 int mla_decode_combine(const void* o_partial, const float* lse_partial, const int32_t* seq_lens,
                        int B, int n_q, int H, int max_blocks, int pages_per_split, int max_splits,
                        void* out, float* lse, const int32_t* status, void* stream) {
@@ -200,19 +289,9 @@ int mla_decode_combine(const void* o_partial, const float* lse_partial, const in
   if ((int64_t)B * n_q * H * 4 > kMaxGrid) return MLA_ERR_BAD_SHAPE;
   if (B == 0) return MLA_OK;
   if (!o_partial || !lse_partial || !seq_lens || !out || !lse) return MLA_ERR_NULL_PTR;
-  mla::CombineArgs a;
-  a.o_part = static_cast<const uint16_t*>(o_partial);
-  a.lse_part = lse_partial;
-  a.seq_lens = seq_lens;
-  a.out = static_cast<uint16_t*>(out);
-  a.lse = lse;
-  a.status = status;
-  a.B = B;
-  a.R = n_q * H;
-  a.max_blocks = max_blocks;
-  a.pps = pages_per_split;
-  a.max_splits = max_splits;
-  const hipError_t e = mla::launch_combine(a, static_cast<hipStream_t>(stream));
+  const hipError_t e = combine_launch(o_partial, lse_partial, seq_lens, B, n_q * H, max_blocks,
+                                      pages_per_split, max_splits, out, lse, status,
+                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

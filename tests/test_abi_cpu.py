@@ -121,6 +121,30 @@ def test_checked_decode_validation(lib):
     assert call(B=0, tags=None, et=None, st=None) == 0
 
 
+def test_noalloc_decode_validation(lib):
+    # the allocation-free call checks its arguments, the scratch limit included,
+    # before any HIP call (the pointers are dummies)
+    P = ctypes.c_void_p
+
+    def call(ms=4, sm=2, B=1, n_q=1, H=64, n_new=1, kv_new=1, out=1, lse=1):
+        Q = lambda v: None if v is None else P(v)  # noqa: E731
+        return lib.mla_decode_paged_append_noalloc(Q(kv_new), n_new, P(1), P(1), P(1), sm, P(1), P(1), B, n_q, H,
+                                                   10, 10, 0.07, 1, ms, Q(out), Q(lse), 1, None)
+
+    rows = 32768
+    assert call(ms=rows // 64 + 1) == 5          # 64 rows x 513 splits > 32768 partial rows
+    assert call(ms=rows // 256 + 1, n_q=4) == 5  # 4 queries x 64 heads x 129 splits
+    assert call(ms=rows // 32 + 1, H=16, n_q=2) == 5
+    assert call(out=None) == 1
+    assert call(lse=None, ms=1) == 1
+    assert call(kv_new=None) == 1
+    assert call(n_new=-1) == 2
+    assert call(sm=0) == 3
+    assert call(H=129) == 2
+    assert call(B=0, kv_new=None, out=None, lse=None) == 0
+    assert lib.mla_status_string(5).startswith(b"split partials exceed")
+
+
 # query rows per decode workgroup: 64 on an FP8 cache, 32 on a BF16 cache
 ROWS = {"fp8": 64, "bf16": 32}
 
