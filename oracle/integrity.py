@@ -26,6 +26,19 @@ Readings taken where the pages leave a step open:
   reads none of its pages (and writes none of its new rows): its output rows
   are 0 with a log-sum-exp of -inf.
 
+The check may also run inside the decode launch, beside the attention, instead
+of in front of it (``stored_rows_ref`` / ``append_checked_ref``).  That form
+reads before it checks: the attention of every request runs on the unchecked
+lengths, and a flagged request is masked afterwards (rows 0, LSE -inf), so it
+still returns no data.  What differs is the store of the step's new rows, which
+cannot wait for the request's verdict.  Reading taken: a new row is stored iff
+the page it goes to passes the check on its own -- the request's length lies in
+``[0, 64 * max_blocks]``, the row's slot is at a position ``>= 0``, and the
+page-map entry of that slot is inside the pool, equals the recorded page (when
+a record is kept) and carries the recorded tag.  So no row ever lands in a page
+that was handed to another owner; a flagged request may still store rows into
+its own pages that pass.
+
 Status bits per request (0 = the request may read the cache):
 """
 
@@ -74,3 +87,59 @@ def check_pages_ref(page_tags, block_table, expected_tags, seq_lens, expected_pa
         status[b] = s
         checked[b] = L if s == 0 else 0
     return status, checked
+
+
+def stored_rows_ref(page_tags, block_table, expected_tags, seq_lens, n_new, expected_pages=None):
+    """Which new rows the in-launch check lets the decode launch store.
+
+    Row ``j`` of request ``b`` sits at ``p = seq_lens[b] - n_new + j``.  It is
+    stored iff ``0 <= seq_lens[b] <= 64 * max_blocks``, ``p >= 0``, and entry
+    ``e = block_table[b, p // 64]`` is in ``[0, num_pages)``, equals
+    ``expected_pages[b, p // 64]`` (if a record is given) and
+    ``page_tags[e] == expected_tags[b, p // 64]``.
+    Returns bool [B, n_new].
+    """
+    page_tags = np.asarray(page_tags, dtype=np.uint32)
+    block_table = np.asarray(block_table, dtype=np.int32)
+    expected_tags = np.asarray(expected_tags, dtype=np.uint32)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    num_pages = page_tags.shape[0]
+    B, max_blocks = block_table.shape
+    keep = np.zeros((B, n_new), dtype=bool)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L < 0 or L > max_blocks * PAGE:
+            continue
+        for j in range(n_new):
+            p = L - n_new + j
+            if p < 0:
+                continue
+            k = p // PAGE
+            page = int(block_table[b, k])
+            if page < 0 or page >= num_pages:
+                continue
+            if expected_pages is not None and page != int(expected_pages[b, k]):
+                continue
+            if int(page_tags[page]) != int(expected_tags[b, k]):
+                continue
+            keep[b, j] = True
+    return keep
+
+
+def append_checked_ref(new_bits, cache, scales, block_table, seq_lens, scale_mode, tensor_scale,
+                       page_tags, expected_tags, expected_pages=None):
+    """The cache after a decode launch that carries the page check: the new rows
+    ``stored_rows_ref`` keeps, written in place one by one as the plain append
+    (``oracle.mla.append_ref``) writes them; the others are dropped."""
+    from oracle import mla as omla
+
+    B, n_new = int(new_bits.shape[0]), int(new_bits.shape[1])
+    keep = stored_rows_ref(page_tags, block_table, expected_tags, seq_lens, n_new, expected_pages)
+    for b in range(B):
+        for j in range(n_new):
+            if keep[b, j]:
+                p = int(seq_lens[b]) - n_new + j
+                # one row, one request whose length ends right after it
+                omla.append_ref(new_bits[b:b + 1, j:j + 1], cache, scales, block_table[b:b + 1],
+                                np.asarray([p + 1], dtype=np.int32), scale_mode, tensor_scale)
+    return keep

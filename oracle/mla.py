@@ -203,15 +203,26 @@ def append_ref(new_bits, cache, scales, block_table, seq_lens, scale_mode, tenso
     Row ``j`` of request ``b`` (of ``n_new``) goes to position
     ``p = seq_lens[b] - n_new + j``: slot ``p % 64`` of page
     ``block_table[b][p // 64]``.  Per-token scales go to ``scales[page, slot]``.
+
+    A row is written only where that slot exists: ``0 <= p < 64 * max_blocks``
+    and a page id inside ``[0, num_pages)``.  Other rows are dropped (the pages
+    say nothing of malformed page maps; the plainest reading is that a row with
+    no slot of its own is not stored anywhere).
     """
     B, n_new = int(new_bits.shape[0]), int(new_bits.shape[1])
+    num_pages = cache.shape[0]
+    cap = block_table.shape[1] * PAGE
     codes, sc = quantize_rows(new_bits.reshape(B * n_new, D), scale_mode, tensor_scale)
     codes = codes.reshape(B, n_new, D)
     sc = sc.reshape(B, n_new)
     for b in range(B):
         for j in range(n_new):
             p = int(seq_lens[b]) - n_new + j
+            if p < 0 or p >= cap:
+                continue
             page = int(block_table[b, p // PAGE])
+            if page < 0 or page >= num_pages:
+                continue
             cache[page, p % PAGE] = codes[b, j]
             if scale_mode == "token":
                 scales[page, p % PAGE] = sc[b, j]

@@ -128,6 +128,31 @@ def oracle_state(w: synth.Workload, requests=None):
     return cache, scales, ts
 
 
+def oracle_pool(w: synth.Workload):
+    """The oracle's quantised pool, every page, before the step's append:
+    (codes [num_pages, 64, 576], per-token scales [num_pages, 64], tensor scale)."""
+    ts = w.tensor_scale() if w.scale_mode == "tensor" else None
+    cache = np.zeros((w.num_pages, 64, 576), np.uint8)
+    scales = np.zeros((w.num_pages, 64), np.float32)
+    for c0 in range(0, w.num_pages, 2048):
+        sel = np.arange(c0, min(c0 + 2048, w.num_pages))
+        codes, sc = omla.fill_pages_ref(w.page_bits(sel), w.scale_mode, ts)
+        cache[sel] = codes
+        scales[sel] = sc
+    return cache, scales, ts
+
+
+def assert_cache_equals(g: "GpuState", cache: np.ndarray, scales: np.ndarray, tag=""):
+    """The GPU cache (and per-token scales) byte for byte as the oracle's."""
+    got = g.cache.cpu().numpy()
+    bad = np.nonzero((got != cache).any(axis=2))
+    assert bad[0].size == 0, f"{tag}: cache rows differ at (page, slot) {list(zip(*bad))[:8]}"
+    if g.scale_mode == "token":
+        gs = g.kv_scale.cpu().numpy()
+        assert np.array_equal(gs.view(np.uint32), scales.view(np.uint32)), f"{tag}: scales differ"
+    log(f"{tag}: cache and scales equal the oracle's")
+
+
 def oracle_decode(w: synth.Workload, requests=None):
     cache, scales, ts = oracle_state(w, requests)
     return omla.decode_ref(w.q_bits(), cache, scales, w.block_table, w.seq_lens, n_q=w.n_q, H=w.H,

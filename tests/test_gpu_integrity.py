@@ -12,9 +12,10 @@ import torch
 
 import synth
 from oracle import integrity as oi
+from oracle import mla as omla
 from synth import integrity as si
 
-from _gpu import GpuState, bf16_tensor_to_f64, compare, log, oracle_decode
+from _gpu import GpuState, assert_cache_equals, bf16_tensor_to_f64, compare, log, oracle_decode, oracle_pool
 
 pytestmark = pytest.mark.gpu
 
@@ -158,6 +159,16 @@ def test_flagged_request_is_aborted_within_the_step(mode):
     l = lse.detach().cpu().double().numpy()
     assert not o[victim].any() and np.all(np.isneginf(l[victim]))
     assert torch.equal(g.cache[page], before), "an aborted request wrote into the cache"
+    # the cache after the step: in front of the decode, the check zeroes a flagged
+    # request's length, so none of its rows is stored; inside the launch each row
+    # is stored iff its own page passes
+    cache, scales, ts = oracle_pool(w)
+    if check_mode == "launch":
+        oi.append_checked_ref(w.new_row_bits(), cache, scales, w.block_table, w.seq_lens, w.scale_mode, ts,
+                              tags, et)
+    else:
+        omla.append_ref(w.new_row_bits(), cache, scales, w.block_table, want_l, w.scale_mode, ts)
+    assert_cache_equals(g, cache, scales, f"e2e {name}")
     keep = [0, 2, 3]
     ref_o, ref_l = oracle_decode(w, requests=keep)
     compare(o, l, ref_o, ref_l, requests=keep, tag=f"e2e {name}")
@@ -239,8 +250,6 @@ def test_in_launch_check_with_an_earlier_stale_page():
     not the one its new row goes to: the row is stored into its own last page
     (which passes), the stale page is left alone, and the request's rows still
     come out 0 / -inf while the others match the oracle."""
-    import long_context_mla_amd as mla
-
     w, tags, et, victim, last_page = _e2e_workload()
     tags[last_page] ^= np.uint32(1)  # undo: the last page passes again
     first_page = int(w.block_table[victim, 0])
@@ -258,14 +267,13 @@ def test_in_launch_check_with_an_earlier_stale_page():
     l = lse.detach().cpu().double().numpy()
     assert not o[victim].any() and np.all(np.isneginf(l[victim]))
     assert torch.equal(g.cache[first_page], before)
-    # the victim's new row went to its own last page, as a check-free append puts it
-    ref = GpuState(w)
-    ref_st = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(), ref.device,
-                            pages_per_split=st.pps, max_splits=st.max_splits, cache_dtype=w.cache_dtype)
-    ref_st(ref.q, ref.cache, ref.kv_scale, ref.scale_mode, ref.block_table, ref.seq_lens, w.softmax_scale,
-           new_rows=ref.new_rows)
-    torch.cuda.synchronize()
-    assert torch.equal(g.cache, ref.cache) and torch.equal(g.kv_scale, ref.kv_scale)
+    # the victim's new row went to its own last page, which passes: the cache
+    # and scales are byte for byte the oracle's store rule for the in-launch check
+    cache, scales, ts = oracle_pool(w)
+    kept = oi.append_checked_ref(w.new_row_bits(), cache, scales, w.block_table, w.seq_lens, w.scale_mode, ts,
+                                 tags, et)
+    assert kept[victim].all()
+    assert_cache_equals(g, cache, scales, "in-launch, earlier stale page")
     keep = [0, 2, 3]
     ref_o, ref_l = oracle_decode(w, requests=keep)
     compare(o, l, ref_o, ref_l, requests=keep, tag="in-launch, earlier stale page")
@@ -314,6 +322,71 @@ def test_in_launch_status_matches_oracle():
         if want_s[b]:
             assert not o[b].any() and np.all(np.isneginf(l[b])), b
     assert torch.equal(g.cache[stale5], before), "a row was stored into a page that failed the check"
+    cache, scales, ts = oracle_pool(w)
+    oi.append_checked_ref(w.new_row_bits(), cache, scales, bt_h, lens, w.scale_mode, ts, tags, et, ep)
+    assert_cache_equals(g, cache, scales, "in-launch status")
     keep = [4, 6]
     ref_o, ref_l = oracle_decode(w, requests=keep)
     compare(o, l, ref_o, ref_l, requests=keep, tag="in-launch status")
+
+
+PATHS = [("fused", True, None), ("separate", False, None), ("in_launch", True, "launch")]
+
+
+@pytest.mark.parametrize("path", PATHS, ids=[p[0] for p in PATHS])
+def test_rows_without_a_slot_are_not_stored(path):
+    """New rows with no slot of their own: a request whose page map is full and
+    whose length is the map's capacity + 2 (of its three rows, only the first
+    has a slot), and a request whose page-map entry at the append position is
+    -1 (a clamp would name page 0).  The cache and scales after the step equal
+    the oracle's byte for byte: the plain append (fused into the decode launch,
+    or a launch of its own) stores exactly the rows with a slot; the in-launch
+    check stores nothing for the request flagged for its length or its page."""
+    import long_context_mla_amd as mla
+
+    name, fuse_append, check_mode = path
+    w = synth.custom("no_slot", B=3, n_q=1, H=16, context_lens=(300, 100, 200), append=3, cache_dtype="fp8",
+                     scale_mode="token", seed=18)
+    cap = w.max_blocks * 64
+    bt = w.block_table.copy()
+    lens = w.seq_lens.copy()
+    assert (bt[0] >= 0).all(), "request 0 must have a full page map"
+    lens[0] = cap + 2
+    assert (int(lens[1]) - 3) // 64 == (int(lens[1]) - 1) // 64 == 1
+    # page 0 is no row's own target here (the seed is chosen so), so any write to it is a clamped -1
+    assert 0 not in (bt[0, -1], bt[1, 1], bt[2, (int(lens[2]) - 1) // 64])
+    bt[1, 1] = -1
+    g = GpuState(w)
+    g.block_table = _dev(bt)
+    g.seq_lens = _dev(lens)
+    page0 = g.cache[0].clone()
+    scale0 = g.kv_scale[0].clone()
+    npg = -(-cap // 64) + 1
+    st = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(lens.max()), int(lens.sum()), g.device,
+                        pages_per_split=2, max_splits=-(-npg // 2), fuse_append=fuse_append,
+                        check_mode=check_mode or "front", cache_dtype="fp8")
+    page_check = None
+    tags = et = None
+    if check_mode:
+        tags = np.arange(1, w.num_pages + 1, dtype=np.uint32)
+        et = np.where(bt >= 0, tags[np.clip(bt, 0, w.num_pages - 1)], 0).astype(np.uint32)
+        page_check = (_dev(tags), _dev(et), None)
+    out, lse = st(g.q, g.cache, g.kv_scale, g.scale_mode, g.block_table, g.seq_lens, w.softmax_scale,
+                  new_rows=g.new_rows, page_check=page_check)
+    torch.cuda.synchronize()
+    log(f"no-slot {name}: cap={cap} lens={lens.tolist()} splits={st.max_splits}")
+    assert torch.equal(g.cache[0], page0) and torch.equal(g.kv_scale[0], scale0), "page 0 was written"
+    cache, scales, ts = oracle_pool(w)
+    if check_mode:
+        kept = oi.append_checked_ref(w.new_row_bits(), cache, scales, bt, lens, "token", ts, tags, et)
+        assert not kept[0].any() and not kept[1].any() and kept[2].all()
+        want_s, _ = oi.check_pages_ref(tags, bt, et, lens)
+        assert st.status.cpu().numpy().tolist() == want_s.tolist() == [oi.BAD_LEN, oi.OUT_OF_RANGE, 0]
+    else:
+        omla.append_ref(w.new_row_bits(), cache, scales, bt, lens, "token", ts)
+        # the first row of request 0 went to the last slot of its last page
+        assert np.array_equal(cache[bt[0, -1], 63], g.cache[bt[0, -1], 63].cpu().numpy())
+    assert_cache_equals(g, cache, scales, f"no-slot {name}")
+    ref_o, ref_l = oracle_decode(w, requests=[2])
+    compare(bf16_tensor_to_f64(out), lse.detach().cpu().double().numpy(), ref_o, ref_l, requests=[2],
+            tag=f"no-slot {name}")
