@@ -118,6 +118,18 @@ int kv_append_fp8(const void* kv_new, void* kv_cache, float* kv_scale, int scale
 /*
  * mla_decode_paged — split-KV decode attention over the paged latent cache.
  *
+ * MLA keeps one latent head that every query head attends to; when the cache
+ * of a request is cut by sequence, each part computes a partial attention
+ * output with its log-sum-exp, and the parts are merged with online softmax
+ * ("vLLM x AgentX: Optimizing for Real-World Agentic Serving", section
+ * "Model-specific parallelism / Kimi K3", where the parts sit on different
+ * GPUs).  Here the parts are splits of one request's pages on one GPU:
+ * for row r of request b and split s over its visible tokens T_s,
+ *   lse_s = ln sum_{t in T_s} exp(c q_r.k_t),
+ *   o_s   = sum_{t in T_s} exp(c q_r.k_t - lse_s) v_t,
+ * with k_t the whole 576-element row, v_t its first 512 elements and
+ * c = softmax_scale; mla_decode_combine merges the splits.
+ *
  *   q           bf16 [B, n_q, H, 576]: the query already absorbed into the
  *               latent space (latent 512 | rope 64).
  *   kv_cache    MLA_CACHE_FP8_E4M3: e4m3 codes [num_pages, 64, 576];

@@ -69,7 +69,35 @@ def test_decode_argument_validation(lib):
     assert _decode(lib, dt=7) == 3
     assert _decode(lib, sm=5) == 3
     assert _decode(lib, dt=0, sm=1) == 3  # bf16 cache takes no scale
+    assert _decode(lib, pps=2**16, ms=2**15, op=1, lp=1) == 2  # split starts would pass 2^31
+    assert _decode(lib, pps=2**16 - 1, ms=2**15, op=1, lp=1, B=0) == 0  # just inside, nothing to do
     assert _decode(lib, B=0) == 0  # empty batch: nothing to do
+
+
+def test_binding_checks_the_scale_shape():
+    # the binding rejects a scale array of the wrong shape before calling the library
+    import torch
+
+    import long_context_mla_amd as mla
+
+    q = torch.zeros((1, 1, 64, 576), dtype=torch.bfloat16)
+    cache = torch.zeros((4, 64, 576), dtype=torch.uint8)
+    bt = torch.zeros((1, 4), dtype=torch.int32)
+    sl = torch.ones(1, dtype=torch.int32)
+    out = torch.empty((1, 1, 64, 512), dtype=torch.bfloat16)
+    lse = torch.empty((1, 1, 64), dtype=torch.float32)
+    for mode, scale in (("token", torch.ones((3, 64))), ("token", torch.ones(256)), ("tensor", torch.ones(2))):
+        with pytest.raises(ValueError, match="kv_scale"):
+            mla.mla_decode_paged(q, cache, scale, mode, bt, sl, 0.07, 4, 1, out=out, lse=lse)
+    assert mla.mla_decode_paged_append_noalloc is not None
+    with pytest.raises(ValueError, match="kv_scale"):
+        mla.mla_decode_paged_append_noalloc(torch.zeros((1, 1, 576), dtype=torch.bfloat16), q, cache,
+                                            torch.ones((4, 63)), "token", bt, sl, 0.07, 4, 1, out, lse)
+
+
+def test_combine_rejects_split_overflow(lib):
+    P = ctypes.c_void_p
+    assert lib.mla_decode_combine(P(1), P(1), P(1), 1, 1, 1, 1, 2**16, 2**15, P(1), P(1), None, None) == 2
 
 
 def test_append_and_combine_validation(lib):

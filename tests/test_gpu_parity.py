@@ -32,6 +32,15 @@ CASES = [
          scale_mode="token"),
     dict(name="fp8_empty_req", B=2, n_q=1, H=64, context_lens=(0, 100), cache_dtype="fp8",
          scale_mode="token", append=0),
+    # the header's limits: H up to 128, n_q up to 8 (up to 16 row groups of 64 on FP8,
+    # 32 of 32 on BF16), full and ragged last pages
+    dict(name="fp8_h128", B=2, n_q=1, H=128, context_lens=(2000, 63), cache_dtype="fp8", scale_mode="token"),
+    dict(name="fp8_nq5_h64", B=2, n_q=5, H=64, context_lens=(1019, 3), cache_dtype="fp8", scale_mode="token"),
+    dict(name="fp8_nq8_h128", B=1, n_q=8, H=128, context_lens=(632,), cache_dtype="fp8", scale_mode="tensor"),
+    dict(name="fp8_nq8_h16", B=3, n_q=8, H=16, context_lens=(56, 0, 300), cache_dtype="fp8", scale_mode="token"),
+    dict(name="bf16_h128", B=2, n_q=1, H=128, context_lens=(640, 77), cache_dtype="bf16"),
+    dict(name="bf16_nq5_h64", B=1, n_q=5, H=64, context_lens=(333,), cache_dtype="bf16"),
+    dict(name="bf16_nq8_h128", B=1, n_q=8, H=128, context_lens=(256,), cache_dtype="bf16"),
 ]
 
 
@@ -335,3 +344,31 @@ def test_restart_on_late_large_scores(cache_dtype):
     for pps, ms in [(npg, 1), (20, -(-npg // 20)), (1, npg)]:
         o, l = g.decode_only(pps, ms)
         compare(o, l, ref_o, ref_l, tag=f"restart {cache_dtype} pps={pps} splits={ms}")
+
+
+@pytest.mark.parametrize("cache_dtype", ["fp8", "bf16"])
+def test_five_score_jumps_in_one_split(cache_dtype):
+    """Five keys along one head's query, in five later pages of one split, the
+    first about 77 log2-units above the first page's maximum and each next one 80
+    above the one before (so each would push a weight past 2^64 of the reference
+    in force when it is met).  The FP8 kernel switches
+    to a scan at the first and reruns once with the split's true maxima; the BF16
+    kernel restarts four times and takes the fifth jump with weights near 2^80,
+    still finite.  Both match the oracle.  q is N(0, 6) so that the jumps need
+    only small keys (the winning value row stays near N(0, 1))."""
+    lens = (2000,)
+    per_gain = 0.072168784 * 36.0 * 576 / np.log(2.0)  # log2-units of score per unit of gain
+    gains = [(20.0 + 80.0 * k) / per_gain for k in range(1, 6)]  # 100, 180, ..., 420 log2-units
+    needles = tuple((0, t, 5, g) for t, g in zip((100, 500, 900, 1300, 1700), gains))
+    kw = dict(scale_mode="token", append=1) if cache_dtype == "fp8" else {}
+    w = synth.custom(f"jumps5_{cache_dtype}", B=1, n_q=1, H=64, context_lens=lens, cache_dtype=cache_dtype,
+                     seed=13, sigma_q=6.0, needles=needles, **kw)
+    g = GpuState(w)
+    ref_o, ref_l = oracle_decode(w)
+    out, lse = g.step()
+    summ = compare(out, lse, ref_o, ref_l, tag=f"five jumps {cache_dtype} planned")
+    assert summ["max_ref"] > 1.0  # the last needle owns head 5
+    npg = int(-(-w.seq_lens.max() // 64))
+    for pps, ms in [(npg, 1), (16, 2)]:
+        o, l = g.decode_only(pps, ms)
+        compare(o, l, ref_o, ref_l, tag=f"five jumps {cache_dtype} pps={pps} splits={ms}")
