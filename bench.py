@@ -5,8 +5,10 @@ A step is the whole hot path on one batch: the step's new latent rows go into
 the FP8 cache and the split-KV decode runs in one launch
 (mla_decode_paged_append: kv_append_fp8 + mla_decode_paged), then
 mla_decode_combine (--separate-append issues kv_append_fp8 on its own).  Steps are
-timed twice, launched eagerly and as replays of one HIP graph per step (a serving
-loop's form); the step time is the faster of the two, both reported.  The decode
+timed twice, launched eagerly and as replays of HIP graphs that each hold one
+step on every rotated cache in turn (a serving loop's form: a model's
+consecutive layers, each with its own cache, in one graph); the step time is
+the faster of the two, both reported.  The decode
 kernel's own duration comes from HIP events around a burst of back-to-back
 decode launches, and, for its spread, around every launch of the eager pass
 (--no-graph times eager steps only).  The default
@@ -60,7 +62,7 @@ def parse():
     ap.add_argument("--separate-append", action="store_true",
                     help="kv_append_fp8 as its own launch before mla_decode_paged")
     ap.add_argument("--no-graph", action="store_true",
-                    help="time eager launches instead of one HIP graph per step")
+                    help="time eager launches only (no HIP graphs)")
     ap.add_argument("--no-page-check", action="store_true",
                     help="skip timing the KV page-tag check in front of the step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -349,24 +351,39 @@ def main():
     torch.cuda.synchronize()
     k_us_burst = start.elapsed_time(end) / args.steps * 1000
     if not args.no_graph:
-        # Pass 2: each step (append, decode, combine) as one HIP graph per
-        # rotated cache, replayed back to back as a serving loop would.
-        graphs = []
+        # Pass 2: the steps as HIP graphs replayed back to back, as a serving
+        # loop runs a model's layers: one graph holds one step on each rotated
+        # cache in turn (consecutive layers, each with its own cache), so the
+        # host's launch cost is paid once per `rotate` steps.  A step count
+        # that is not a multiple of that ends with a shorter graph.
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
+        graphs = []      # one step per graph (the page-check comparison below)
+        multi = {}       # steps per graph -> graph of that many consecutive steps
         with torch.cuda.stream(cap):
             for k in range(args.rotate):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cap):
                     run(k, st=cap)
                 graphs.append(g)
+            for n in {args.rotate, args.warmup % args.rotate, args.steps % args.rotate} - {0}:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    for k in range(n):
+                        run(k, st=cap)
+                multi[n] = g
         stream.wait_stream(cap)
-        for i in range(args.warmup):
-            graphs[i % args.rotate].replay()
+
+        def replay_steps(n):
+            for _ in range(n // args.rotate):
+                multi[args.rotate].replay()
+            if n % args.rotate:
+                multi[n % args.rotate].replay()
+
+        replay_steps(args.warmup)
         torch.cuda.synchronize()
         start.record(stream)
-        for i in range(args.steps):
-            graphs[(args.warmup + i) % args.rotate].replay()
+        replay_steps(args.steps)
         end.record(stream)
         torch.cuda.synchronize()
         ms_step_graph = start.elapsed_time(end) / args.steps
@@ -434,8 +451,8 @@ def main():
         "hbm_tb_s_step": round(alg_bytes / (ms_step * 1e-3) / 1e12, 3),
         "roofline_frac_step": round(max(t_hbm, t_mfma) / (ms_step * 1e-3), 4),
         "decode_kernel_us_p10_p50_p90": [round(float(np.percentile(k_ms, p)) * 1000, 2) for p in (10, 50, 90)],
-        "step_launch": ("hip graph per step" if ms_step_graph is not None and ms_step_graph <= ms_step_eager
-                        else "eager launches"),
+        "step_launch": (f"hip graphs of {args.rotate} steps (one per rotated cache)"
+                        if ms_step_graph is not None and ms_step_graph <= ms_step_eager else "eager launches"),
         "ms_per_step_graph": None if ms_step_graph is None else round(ms_step_graph, 5),
         "append": "separate kv_append_fp8 launch" if args.separate_append or w.n_new == 0
                   else "in the decode launch (mla_decode_paged_append)",

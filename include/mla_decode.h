@@ -28,6 +28,9 @@
  *   query i sees tokens t < L_b - n_q + i + 1 (causal among the new tokens).
  *   Query / output row r = i * H + h.
  *   E4M3 is the OCP E4M3FN encoding (bias 7, no infinities, max 448).
+ *   Alignment: q, kv_cache, kv_new, o_partial and out must be 16-byte aligned
+ *   (the kernels move 16-byte pieces); the other arrays need the alignment of
+ *   their element type.
  *
  * Ownership and threading: the caller owns every buffer; the library never
  * allocates, frees or synchronises (the one buffer it owns, the static

@@ -94,6 +94,10 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+# arrays the kernels move in 16-byte pieces
+_ALIGN16 = ("q", "kv_cache", "kv_new", "o_partial", "out")
+
+
 def _need(t, name, dtype, device=None, ndim=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -105,6 +109,8 @@ def _need(t, name, dtype, device=None, ndim=None):
         raise ValueError(f"{name} must be on {device}, got {t.device}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if name in _ALIGN16 and t.data_ptr() % 16:
+        raise ValueError(f"{name} must be 16-byte aligned")
 
 
 def _check(fn, status):

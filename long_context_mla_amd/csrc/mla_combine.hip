@@ -3,48 +3,59 @@
 // by peers ("vLLM x AgentX: Optimizing for Real-World Agentic Serving", section
 // "Model-specific parallelism / Kimi K3"), here applied to the splits of one GPU.
 //
-// One workgroup per (request, row, 128-dim chunk).  The split weights
-// exp(lse_s - max_s lse_s) are computed once, in parallel, into LDS; then 8
-// groups of 32 lanes (one float4 of the chunk per lane) stride over the splits
-// with several loads in flight, and an LDS reduction folds the 8 groups.
+// One workgroup per (request, row, 128-dim chunk), 256 threads: 16 groups of
+// 16 lanes, each lane one 16-byte piece (8 values) of the chunk.  Up to 512
+// splits every lane loads all of its group's partials (splits g, g + 16, ...)
+// at once, together with the split LSEs, before anything depends on them: one
+// memory round trip.  The split weights exp(lse_s - max_s lse_s) go through
+// LDS, each lane sums its splits from registers, and an LDS reduction folds
+// the 16 groups.  More splits than that stream through in blocks.
 #include "device_common.h"
 #include "launch.h"
 
 namespace mla {
 
-constexpr int kWeightChunk = 1024;  // split weights held in LDS at a time
-constexpr int kHeldSplits = 128;   // splits whose partials a lane holds in registers at once
+constexpr int kGroups = 16;                  // split groups per workgroup
+constexpr int kHeldSplits = kGroups * 32;    // splits whose partials lanes hold at once
+constexpr int kWeightChunk = 1024;           // split weights held in LDS at a time (streaming)
 
-// Four consecutive bf16 partial values (8 bytes) as floats (exact).
-__device__ __forceinline__ f32x4 load_bf16x4(const uint16_t* p) {
-  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
-  return f32x4{float_of(w.x << 16), float_of(w.x & 0xffff0000u), float_of(w.y << 16), float_of(w.y & 0xffff0000u)};
+// Eight consecutive bf16 partial values (16 bytes) added to acc with weight w (exact widening).
+__device__ __forceinline__ void fma_bf16x8(f32x4 (&acc)[2], float w, u32x4 v) {
+  acc[0] += w * f32x4{float_of(v.x << 16), float_of(v.x & 0xffff0000u), float_of(v.y << 16),
+                      float_of(v.y & 0xffff0000u)};
+  acc[1] += w * f32x4{float_of(v.z << 16), float_of(v.z & 0xffff0000u), float_of(v.w << 16),
+                      float_of(v.w & 0xffff0000u)};
 }
 
-// The merge of one (request, row, chunk) when its n_b splits fit NK loads per
-// lane (8 * NK >= n_b >= 1): lane group g = t / 32 loads splits g + 8k (the
-// ones past n_b repeat split n_b - 1, a finite partial, and take weight 0),
-// all before the block-wide max of the LSEs; then the weights go through LDS
-// and the partials are summed from registers.
-template <int NK>
-__device__ __forceinline__ void merge_held(const uint16_t* o_b, int64_t o_stride, float ls, int n_b,
-                                           float* s_w, float* s_red, f32x4& acc, float& wsum,
-                                           float& M) {
-  const int t = threadIdx.x;
-  const int g = t >> 5;
-  f32x4 o[NK];
-#pragma unroll
-  for (int k = 0; k < NK; ++k) o[k] = load_bf16x4(o_b + min(g + 8 * k, n_b - 1) * o_stride);
-  M = wave_max(ls);
-  if ((t & 63) == 0) s_red[t >> 6] = M;
+__device__ __forceinline__ float block_max(float v, float* s_red) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
   __syncthreads();
-  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  if (t < 8 * NK) s_w[t] = (ls == -INFINITY) ? 0.0f : expf(ls - M);
+  return fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+}
+
+// The merge when the n_b splits fit NK loads per lane (16 * NK >= n_b >= 1):
+// group g loads splits g + 16k (the ones past n_b repeat split n_b - 1, a
+// written partial, and take weight 0).  ls0 / ls1 are this thread's split LSEs
+// (splits t and t + 256), already -inf past n_b.
+template <int NK>
+__device__ __forceinline__ void merge_held(const uint16_t* o_b, int64_t o_stride, float ls0, float ls1,
+                                           int n_b, float* s_w, float* s_red, f32x4 (&acc)[2],
+                                           float& wsum, float& M) {
+  const int t = threadIdx.x;
+  const int g = t >> 4;
+  u32x4 o[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k)
+    o[k] = *reinterpret_cast<const u32x4*>(o_b + min(g + kGroups * k, n_b - 1) * o_stride);
+  M = block_max(fmaxf(ls0, ls1), s_red);
+  s_w[t] = ls0 == -INFINITY ? 0.0f : expf(ls0 - M);
+  if (NK * kGroups > 256) s_w[t + 256] = ls1 == -INFINITY ? 0.0f : expf(ls1 - M);
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < NK; ++k) {
-    const float w = g + 8 * k < n_b ? s_w[g + 8 * k] : 0.0f;
-    acc += w * o[k];
+    const float w = g + kGroups * k < n_b ? s_w[g + kGroups * k] : 0.0f;
+    fma_bf16x8(acc, w, o[k]);
     wsum += w;
   }
 }
@@ -55,58 +66,56 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int b = br / a.R;
   const int r = br - b * a.R;
   const int t = threadIdx.x;
-  const int c4 = t & 31;  // float4 index inside the 128-dim chunk
-  const int g = t >> 5;   // split group
+  const int c = t & 15;  // 16-byte piece of the 128-dim chunk
+  const int g = t >> 4;  // split group
   __shared__ float s_w[kWeightChunk];
   __shared__ float s_red[4];
-  __shared__ f32x4 s_acc[8][32];
-  __shared__ float s_ws[8];
+  __shared__ f32x4 s_acc[kGroups][16][2];
+  __shared__ float s_ws[kGroups];
 
   const float* lse_b = a.lse_part + (int64_t)b * a.max_splits * a.R + r;
-  const uint16_t* o_b = a.o_part + ((int64_t)b * a.max_splits * a.R + r) * kDV + chunk * 128 + c4 * 4;
+  const uint16_t* o_b = a.o_part + ((int64_t)b * a.max_splits * a.R + r) * kDV + chunk * 128 + c * 8;
   const int64_t o_stride = (int64_t)a.R * kDV;
-  // Up to kHeldSplits splits (the usual case) each thread's split LSE is
-  // loaded before the length is known (every entry below max_splits lies in
-  // the buffer; the ones past the request's splits are masked once the length
-  // arrives), and each lane's partials for the request's splits are all
-  // loaded at once: two memory round trips instead of one per pass over the
-  // splits.
+  // Up to kHeldSplits splits (the usual case) the split LSEs are loaded
+  // before the length is known: every entry below max_splits lies in the
+  // buffer, and the ones past the request's splits are masked once the length
+  // arrives.
   const bool held = a.max_splits <= kHeldSplits;
-  float ls_held = -INFINITY;
-  if (held && t < a.max_splits) ls_held = lse_b[(int64_t)t * a.R];
+  float ls0 = -INFINITY, ls1 = -INFINITY;
+  if (held && t < a.max_splits) ls0 = lse_b[(int64_t)t * a.R];
+  if (held && t + 256 < a.max_splits) ls1 = lse_b[(int64_t)(t + 256) * a.R];
 
   const int L = min(max(a.seq_lens[b], 0), a.max_blocks * kPage);
   const int n_pages = (L + kPage - 1) / kPage;
   // a request the page check flagged merges no split: its rows come out 0 / -inf
   const int n_b = (a.status && a.status[b]) ? 0 : min(a.max_splits, (n_pages + a.pps - 1) / a.pps);
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   float wsum = 0.0f;
   float M = -INFINITY;
   if (held) {
-    // Each group of 32 lanes takes splits g, g + 8, ...: ceil(n_b / 8) loads
-    // per lane, rounded up to a power of two so that each count is straight-line
-    // code with every load in flight at once (the count is uniform over the
-    // workgroup).  An empty request (n_b == 0) merges nothing.
-    const float ls = t < n_b ? ls_held : -INFINITY;
-    const int n_k = (n_b + 7) >> 3;
-    if (n_k > 8)
-      merge_held<16>(o_b, o_stride, ls, n_b, s_w, s_red, acc, wsum, M);
+    // ceil(n_b / 16) loads per lane, rounded up to a power of two so that each
+    // count is straight-line code with every load in flight at once (the
+    // count is uniform over the workgroup).  An empty request merges nothing.
+    if (t >= n_b) ls0 = -INFINITY;
+    if (t + 256 >= n_b) ls1 = -INFINITY;
+    const int n_k = (n_b + kGroups - 1) / kGroups;
+    if (n_k > 16)
+      merge_held<32>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
+    else if (n_k > 8)
+      merge_held<16>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
     else if (n_k > 4)
-      merge_held<8>(o_b, o_stride, ls, n_b, s_w, s_red, acc, wsum, M);
+      merge_held<8>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
     else if (n_k > 2)
-      merge_held<4>(o_b, o_stride, ls, n_b, s_w, s_red, acc, wsum, M);
+      merge_held<4>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
     else if (n_k > 1)
-      merge_held<2>(o_b, o_stride, ls, n_b, s_w, s_red, acc, wsum, M);
+      merge_held<2>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
     else if (n_k == 1)
-      merge_held<1>(o_b, o_stride, ls, n_b, s_w, s_red, acc, wsum, M);
+      merge_held<1>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
   } else {
-    for (int s = t; s < n_b; s += 256) M = fmaxf(M, lse_b[(int64_t)s * a.R]);
-    M = wave_max(M);
-    if ((t & 63) == 0) s_red[t >> 6] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-
+    float m = -INFINITY;
+    for (int s = t; s < n_b; s += 256) m = fmaxf(m, lse_b[(int64_t)s * a.R]);
+    M = block_max(m, s_red);
     for (int s0 = 0; s0 < n_b; s0 += kWeightChunk) {
       const int s1 = min(n_b, s0 + kWeightChunk);
       __syncthreads();
@@ -116,39 +125,46 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       }
       __syncthreads();
       int s = s0 + g;
-      for (; s + 24 < s1; s += 32) {
-        const f32x4 o0 = load_bf16x4(o_b + s * o_stride);
-        const f32x4 o1 = load_bf16x4(o_b + (s + 8) * o_stride);
-        const f32x4 o2 = load_bf16x4(o_b + (s + 16) * o_stride);
-        const f32x4 o3 = load_bf16x4(o_b + (s + 24) * o_stride);
-        const float w0 = s_w[s - s0], w1 = s_w[s + 8 - s0], w2 = s_w[s + 16 - s0], w3 = s_w[s + 24 - s0];
-        acc += w0 * o0 + w1 * o1 + w2 * o2 + w3 * o3;
-        wsum += (w0 + w1) + (w2 + w3);
+      for (; s + 3 * kGroups < s1; s += 4 * kGroups) {
+        u32x4 o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = *reinterpret_cast<const u32x4*>(o_b + (s + kGroups * k) * o_stride);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float w = s_w[s + kGroups * k - s0];
+          fma_bf16x8(acc, w, o[k]);
+          wsum += w;
+        }
       }
-      for (; s < s1; s += 8) {
+      for (; s < s1; s += kGroups) {
         const float w = s_w[s - s0];
-        acc += w * load_bf16x4(o_b + s * o_stride);
+        fma_bf16x8(acc, w, *reinterpret_cast<const u32x4*>(o_b + s * o_stride));
         wsum += w;
       }
     }
   }
-  s_acc[g][c4] = acc;
-  if (c4 == 0) s_ws[g] = wsum;
+  s_acc[g][c][0] = acc[0];
+  s_acc[g][c][1] = acc[1];
+  if (c == 0) s_ws[g] = wsum;
   __syncthreads();
   if (g == 0) {
-    f32x4 tot = s_acc[0][c4];
+    f32x4 lo = s_acc[0][c][0], hi = s_acc[0][c][1];
     float wt = s_ws[0];
 #pragma unroll
-    for (int k = 1; k < 8; ++k) {
-      tot += s_acc[k][c4];
+    for (int k = 1; k < kGroups; ++k) {
+      lo += s_acc[k][c][0];
+      hi += s_acc[k][c][1];
       wt += s_ws[k];
     }
     const float inv = wt > 0.0f ? 1.0f / wt : 0.0f;
-    uint16_t* dst = a.out + (int64_t)br * kDV + chunk * 128 + c4 * 4;
-    const uint32_t lo = float_to_bf16(tot[0] * inv) | (uint32_t(float_to_bf16(tot[1] * inv)) << 16);
-    const uint32_t hi = float_to_bf16(tot[2] * inv) | (uint32_t(float_to_bf16(tot[3] * inv)) << 16);
-    *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
-    if (chunk == 0 && c4 == 0) a.lse[br] = wt > 0.0f ? M + logf(wt) : -INFINITY;
+    uint16_t* dst = a.out + (int64_t)br * kDV + chunk * 128 + c * 8;
+    u32x4 v;
+    v.x = float_to_bf16(lo[0] * inv) | (uint32_t(float_to_bf16(lo[1] * inv)) << 16);
+    v.y = float_to_bf16(lo[2] * inv) | (uint32_t(float_to_bf16(lo[3] * inv)) << 16);
+    v.z = float_to_bf16(hi[0] * inv) | (uint32_t(float_to_bf16(hi[1] * inv)) << 16);
+    v.w = float_to_bf16(hi[2] * inv) | (uint32_t(float_to_bf16(hi[3] * inv)) << 16);
+    *reinterpret_cast<u32x4*>(dst) = v;
+    if (chunk == 0 && c == 0) a.lse[br] = wt > 0.0f ? M + logf(wt) : -INFINITY;
   }
 }
 

@@ -95,6 +95,22 @@ def test_binding_checks_the_scale_shape():
                                             torch.ones((4, 63)), "token", bt, sl, 0.07, 4, 1, out, lse)
 
 
+def test_binding_checks_alignment():
+    # q, the cache, the new rows, the partials and the output move in 16-byte pieces
+    import torch
+
+    import long_context_mla_amd as mla
+
+    q = torch.zeros(64 * 576 + 8, dtype=torch.bfloat16)[1:1 + 64 * 576].view(1, 1, 64, 576)
+    cache = torch.zeros((4, 64, 576), dtype=torch.uint8)
+    bt = torch.zeros((1, 4), dtype=torch.int32)
+    sl = torch.ones(1, dtype=torch.int32)
+    out = torch.empty((1, 1, 64, 512), dtype=torch.bfloat16)
+    lse = torch.empty((1, 1, 64), dtype=torch.float32)
+    with pytest.raises(ValueError, match="16-byte aligned"):
+        mla.mla_decode_paged(q, cache, torch.ones(1), "tensor", bt, sl, 0.07, 4, 1, out=out, lse=lse)
+
+
 def test_combine_rejects_split_overflow(lib):
     P = ctypes.c_void_p
     assert lib.mla_decode_combine(P(1), P(1), P(1), 1, 1, 1, 1, 2**16, 2**15, P(1), P(1), None, None) == 2
