@@ -24,7 +24,11 @@ Prints one JSON line: the throughput in KV-tokens/s, plus
 * roofline: the decode kernel's algorithmic bytes per launch / its mean
   duration (HIP events around a burst of back-to-back launches on its
   stream) against 8 TB/s;
-* cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
+* cpu_baseline: the CPU oracle timed on a bounded sample of the same workload
+  (all cores, and one thread), with the host's CPU model;
+* measured_peaks: this GPU's streaming-read, LDS-DMA page-stream and bf16
+  MFMA peaks from the library's microbenchmarks (--no-peaks skips them), and
+  the roofline fraction against them beside the vendor figure.
 """
 
 from __future__ import annotations
@@ -54,6 +58,7 @@ def parse():
     ap.add_argument("--config", default="fp8_single_100k")
     ap.add_argument("--rotate", type=int, default=8, help="distinct cache copies cycled over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak microbenchmarks")
     ap.add_argument("--cpu-repeats", type=int, default=3, help="at least this many oracle runs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="and oracle runs until this much CPU time has passed")
@@ -113,19 +118,31 @@ def load_traffic(workload):
     return d.get("hbm_bytes_per_launch")
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, repeats, seconds):
     """The oracle, as it stands, on the same workload: one full step (append of
-    the new row + attention of every head over the whole context) for request 0."""
+    the new row + attention of every head over the whole context) for request 0,
+    timed with every core numpy's BLAS uses and again with one thread."""
     import numpy as np
 
     from oracle import mla as omla
 
     try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
-    except Exception:  # noqa: BLE001
-        cores = os.cpu_count()
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_info = threadpool_limits = None
+    cores = os.cpu_count()
+    if threadpool_info is not None:
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [cores])
     b = 0
     pages = w.pages_of(b)
     ts = w.tensor_scale() if w.scale_mode == "tensor" else None
@@ -137,18 +154,46 @@ def cpu_baseline(w, repeats, seconds):
     q = w.q_bits()[b:b + 1]
     bt = w.block_table[b:b + 1]
     sl = w.seq_lens[b:b + 1]
-    times = []
-    while len(times) < repeats or sum(times) < seconds:
-        t0 = time.perf_counter()
-        omla.append_ref(new, codes, scales, bt, sl, w.scale_mode, ts)
-        omla.decode_ref(q, codes, scales, bt, sl, n_q=w.n_q, H=w.H, cache_dtype=w.cache_dtype,
-                        scale_mode=w.scale_mode, softmax_scale=w.softmax_scale, tensor_scale=ts)
-        times.append(time.perf_counter() - t0)
+
+    def run(min_runs, budget):
+        times = []
+        while len(times) < min_runs or sum(times) < budget:
+            t0 = time.perf_counter()
+            omla.append_ref(new, codes, scales, bt, sl, w.scale_mode, ts)
+            omla.decode_ref(q, codes, scales, bt, sl, n_q=w.n_q, H=w.H, cache_dtype=w.cache_dtype,
+                            scale_mode=w.scale_mode, softmax_scale=w.softmax_scale, tensor_scale=ts)
+            times.append(time.perf_counter() - t0)
+        return times
+
+    times = run(repeats, seconds)
     t = float(np.median(times))
+    times1 = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            times1 = run(1, 0.0)  # one run: the 1-thread figure is context only
     tokens = int(w.seq_lens[b])
-    return {"value": tokens / t, "unit": "KV-tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"request 0 of {w.name}: append + all {w.H} heads x {tokens} tokens, "
-                      f"median of {len(times)} runs of {t:.2f} s, {sum(times):.1f} s in all (fp64 numpy)"}
+    out = {"value": tokens / t, "unit": "KV-tokens/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"request 0 of {w.name}: append + all {w.H} heads x {w.n_q} queries x {tokens} tokens, "
+                     f"median of {len(times)} runs of {t:.2f} s, {sum(times):.1f} s in all (fp64 numpy)",
+           "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+    if times1:
+        out["value_1thread"] = tokens / float(np.median(times1))
+        out["sample_1thread"] = f"the same request on one thread: {float(np.median(times1)):.2f} s"
+    return out
+
+
+def measured_peaks():
+    """This GPU's own peaks, measured by the library's microbenchmarks
+    (long_context_mla_amd.peaks): a streaming read of 2 GiB (eight times the
+    last-level cache), 36,864-byte pages into LDS by LDS-DMA (the decode
+    kernel's staging) at one workgroup per compute unit, and a bf16 MFMA loop."""
+    from long_context_mla_amd import peaks
+
+    hbm, _ = peaks.hbm_read(grids=(256, 512), reps=5)
+    pages = peaks.page_stream(depths=(2,), reps=5)[2]
+    tflops, ghz = peaks.mfma_bf16(waves_per_simd=2)
+    return {"hbm_read_GBs": round(hbm, 1), "lds_dma_page_stream_GBs": round(pages, 1),
+            "mfma_bf16_TFLOPs": round(tflops, 1), "shader_clock_GHz": round(ghz, 3)}
 
 
 def time_page_check(args, w, mla, torch, np, dev, stream, cap, step, bt, sl, run_checked, graphs):
@@ -461,6 +506,14 @@ def main():
     }
     if page_check is not None:
         line["page_check"] = page_check
+    if not args.no_peaks:
+        mp = measured_peaks()
+        line["measured_peaks"] = mp
+        if bound == "hbm":
+            roof["frac_vs_measured_hbm_read"] = round(achieved_gbs / mp["hbm_read_GBs"], 4)
+            roof["frac_vs_measured_page_stream"] = round(achieved_gbs / mp["lds_dma_page_stream_GBs"], 4)
+        else:
+            roof["frac_vs_measured_mfma"] = round(achieved_tflops / mp["mfma_bf16_TFLOPs"], 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_repeats, args.cpu_seconds)
     print(json.dumps(line), flush=True)

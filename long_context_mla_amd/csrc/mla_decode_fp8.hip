@@ -459,19 +459,23 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   };
   // lane l copies token 16j + l/4, chunk 4i + ((l%4) ^ F) of group i
   const uint32_t goff = (uint32_t)((16 * j + (lane >> 2)) * 576 + (((lane & 3) ^ swz(lane >> 4, j)) << 4));
-  auto dma_page = [&](int it) {
+  // Pieces p0 .. p1-1 of the copy of page it: groups 0..7 of the V part, the
+  // rope part, then (per-token scales) the scales.
+  auto dma_parts = [&](int it, int p0, int p1) {
     if ((it >> 6) != id_chunk) reload_ids(it >> 6);
     const int pg = min(max(__builtin_amdgcn_readlane(ids, it & 63), 0), a.num_pages - 1);
     const uint8_t* src = a.cache + (int64_t)pg * (kPage * kD);
     const uint32_t vdst = lds_addr(s_v + (it % kVBuf) * kVBytes + j * 8192);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) lds_dma16(src + 64 * i, goff, vdst + 1024 * i);
-    lds_dma16(src + 64 * 8, goff, lds_addr(s_rope + (it % kRBuf) * kRBytes + j * 1024));
+    for (int i = 0; i < 8; ++i)
+      if (i >= p0 && i < p1) lds_dma16(src + 64 * i, goff, vdst + 1024 * i);
+    if (8 >= p0 && 8 < p1) lds_dma16(src + 64 * 8, goff, lds_addr(s_rope + (it % kRBuf) * kRBytes + j * 1024));
     // the scales of this wave's own 16 tokens: a row appended in this launch
     // overwrites its scale in LDS after this wave's wait
-    if (SCALE == kScaleToken && lane < 16)
+    if (9 >= p0 && 9 < p1 && SCALE == kScaleToken && lane < 16)
       lds_dma4(a.kv_scale + (int64_t)pg * kPage + 16 * j, lane * 4, lds_addr(&s_scale[(it % kVBuf) * 64 + 16 * j]));
   };
+  auto dma_page = [&](int it) { dma_parts(it, 0, 10); };
 
   // Rows appended in this launch that fall in this wave's quarter of page it:
   // encoded exactly as kv_append_fp8 does and put over the bytes the copy
@@ -631,9 +635,16 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     // page's flags are looked at; a scan then throws it away with the rest.)
     uint32_t fo = flag_word(0);
     for (int it = 1; it <= n_it; ++it) {
-      if (it + 2 < n_it) dma_page(it + 2);
+      // The copy of page it + 2: three pieces before P V of page it - 1, the
+      // rest after it is issued (its buffers were last read by P V of page
+      // it - 2 and QK^T of page it - 1, both before barrier D).  A piece that
+      // waits for room in the memory pipeline then holds up the wave while
+      // the matrix core still works through the queued MFMAs.
+      if (it + 2 < n_it) dma_parts(it + 2, 0, 3);
       phase_fence();
       if (!scan) pv(it - 1);
+      phase_fence();
+      if (it + 2 < n_it) dma_parts(it + 2, 3, 10);
       settle(fo);
       if (allow_scan && fo != 0u) scan = true;
       if (it == n_it) break;
