@@ -3,6 +3,7 @@
 #pragma once
 
 #include "device_common.h"
+#include "launch.h"
 
 namespace mla {
 
@@ -51,10 +52,16 @@ struct SwzBf16 {
 };
 
 // Workgroup -> (request, split, row group).  The hardware hands workgroup i
-// to XCD i % 8.  Work units u = b * max_splits + split go to the XCDs round
-// robin, so every XCD gets an equal share of the units whatever the split
-// count; the n_rg row groups of a unit (which read the same pages) are
-// consecutive workgroups of one XCD and share its L2.  Grid size:
+// to XCD i % 8, in order of i.  Items v = (split * B + b) * n_rg + rg run in
+// split-major order, and within every block of 64 workgroups the 8 x 8
+// (workgroup, XCD) grid is transposed, so items 8c .. 8c+7 all go to XCD c % 8
+// and start together.  Eight consecutive items are then the row groups of a
+// unit and the same split of neighbouring requests: when requests that share
+// a prefix are adjacent in the batch (the page map of each names the same
+// physical pages), their workgroups read each shared page at about the same
+// time on one XCD, and its L2 serves all but the first read.  Each XCD gets
+// an equal share of the items; a last block of fewer than 64 workgroups, and
+// a batch of one request, go round robin.  Grid size:
 // decode_grid_size(B, max_splits, n_rg).
 struct WorkUnit {
   int b, split, rg;
@@ -62,13 +69,15 @@ struct WorkUnit {
 };
 __device__ __forceinline__ WorkUnit decode_work_unit(int B, int max_splits, int n_rg) {
   const int id = blockIdx.x;
-  const int j = id >> 3;
-  const int u = (j / n_rg) * 8 + (id & 7);
+  const int grid = (int)decode_grid_size(B, max_splits, n_rg);
+  const int full = B > 1 ? grid & ~63 : 0;  // one request shares no pages: round robin throughout
+  const int v = id < full ? (id & ~63) | ((id & 7) << 3) | ((id >> 3) & 7) : id;
+  const int u = v / n_rg;
   WorkUnit w;
-  w.rg = j % n_rg;
+  w.rg = v - u * n_rg;
   w.valid = u < B * max_splits;
-  w.b = w.valid ? u / max_splits : 0;
-  w.split = w.valid ? u - w.b * max_splits : 0;
+  w.split = w.valid ? u / B : 0;
+  w.b = w.valid ? u - w.split * B : 0;
   return w;
 }
 

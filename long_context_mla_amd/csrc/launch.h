@@ -74,7 +74,7 @@ int decode_rows_fp8();
 
 // Workgroups of a decode launch (a 1-D grid): the B * max_splits work units
 // (request, split) padded to a multiple of the 8 XCDs, n_rg row groups each.
-inline int64_t decode_grid_size(int64_t B, int64_t max_splits, int64_t n_rg) {
+__host__ __device__ inline int64_t decode_grid_size(int64_t B, int64_t max_splits, int64_t n_rg) {
   return (B * max_splits + 7) / 8 * 8 * n_rg;
 }
 

@@ -17,7 +17,8 @@ def _sample(w):
     L = w.seq_lens
     picks = {int(np.argmin(L)), int(np.argmax(L)), 0, w.B - 1}
     if w.name == "fp8_prefix_shared_b32":
-        picks |= {1, 8, 9}  # two members of one sharing group and another group
+        # every sharer of group 0, two members of group 1 and of group 2
+        picks |= set(range(8)) | {8, 9, 16, 17}
     return sorted(picks)
 
 
