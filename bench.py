@@ -466,7 +466,9 @@ def main():
         "frac": round((achieved_gbs / HBM_PEAK_GBS) if bound == "hbm"
                       else (achieved_tflops / MFMA_BF16_PEAK_TFLOPS), 4),
         "traffic": load_traffic(w.name),
-        "kernel": "decode_fp8_kernel (mla_decode_paged_append)",
+        "kernel": ("decode_fp8_kernel (mla_decode_paged_append)" if fp8 and new_rows is not None
+                   and not args.separate_append else
+                   "decode_fp8_kernel (mla_decode_paged)" if fp8 else "decode_bf16_kernel (mla_decode_paged)"),
         "kernel_us": round(k_us_burst, 3),
         "kernel_us_event_pair": round(k_us, 3),
         "algorithmic_bytes": int(alg_bytes),
@@ -499,8 +501,9 @@ def main():
         "step_launch": (f"hip graphs of {args.rotate} steps (one per rotated cache)"
                         if ms_step_graph is not None and ms_step_graph <= ms_step_eager else "eager launches"),
         "ms_per_step_graph": None if ms_step_graph is None else round(ms_step_graph, 5),
-        "append": "separate kv_append_fp8 launch" if args.separate_append or w.n_new == 0
-                  else "in the decode launch (mla_decode_paged_append)",
+        "append": ("none (the step's rows are already in the cache)" if w.n_new == 0
+                   else "separate kv_append_fp8 launch" if args.separate_append
+                   else "in the decode launch (mla_decode_paged_append)"),
         "ms_per_step_eager": round(ms_step_eager, 5),
         "setup_s": round(t_setup, 1),
     }

@@ -62,7 +62,7 @@ extern "C" {
 #define MLA_VALUE_DIM 512
 #define MLA_PAGE_SIZE 64
 #define MLA_MAX_HEADS 128
-#define MLA_MAX_QUERIES 8
+#define MLA_MAX_QUERIES 2048
 
 typedef enum {
   MLA_OK = 0,
@@ -155,8 +155,11 @@ int kv_append_fp8(const void* kv_new, void* kv_cache, float* kv_scale, int scale
  * partial buffers may be NULL.  With max_splits > 1 only the partials are
  * written (splits past a request's last page are left untouched) and
  * mla_decode_combine must run next; out and lse may then be NULL.
- * Supported: 1 <= H <= 128, 1 <= n_q <= 8.  A row that sees no token gets
- * out = 0 and lse = -inf.
+ * Supported: 1 <= H <= 128, 1 <= n_q <= 2048: a decode step's few new
+ * tokens, or an extend / prefill chunk of up to 2048 new tokens, causal among
+ * themselves, over the cached context (each group of 64 query rows on an FP8
+ * cache, 32 on a BF16 cache, is a workgroup of its own that reads the pages of
+ * its split).  A row that sees no token gets out = 0 and lse = -inf.
  */
 int mla_decode_paged(const void* q, const void* kv_cache, int cache_dtype, const float* kv_scale,
                      int scale_mode, const int32_t* block_table, const int32_t* seq_lens, int B,

@@ -353,10 +353,12 @@ int mla_decode_plan_lens(const int32_t* seq_lens, int B, int n_q, int H, int num
     return u * n_rg;
   };
   // Estimated duration of a plan, in page times.  Workgroup i goes to XCD
-  // i % 8 and waits there for the first of its num_cus / 8 compute units to
-  // come free (one workgroup per unit at a time); it costs its pages plus a
-  // small fixed start and end.  (Fitted by measurement on MI355X: with this
-  // model the plan it ranks first was the fastest measured on every batched
+  // i % 8, in order of i, and works on item decode_item(i) (the kernels'
+  // order); it waits there for the first of its num_cus / 8 compute units to
+  // come free (one workgroup per unit at a time) and costs its pages plus a
+  // small fixed start and end.  Workgroups past a request's last page exit at
+  // once and are skipped.  (Fitted by measurement on MI355X: with this model
+  // the plan it ranks first was the fastest measured on every batched
   // workload.)
   constexpr int64_t kFixedPages = 2;
   const int per_xcd = std::max(1, num_cus / 8);
@@ -366,23 +368,19 @@ int mla_decode_plan_lens(const int32_t* seq_lens, int B, int n_q, int H, int num
     std::vector<MinHeap> free_at(8);
     for (auto& h : free_at)
       for (int c = 0; c < per_xcd; ++c) h.push(0);
-    // Unit u = b * ms + split is launched on XCD u % 8, the units of an XCD in
-    // increasing u (its n_rg workgroups back to back); units past a request's
-    // last page exit at once and are skipped.  The cost is linear in the
-    // number of working units, whatever the grid size.
     int64_t end = 0;
-    for (int b = 0; b < B; ++b) {
-      const int n_units = std::max(1, (pages[b] + pps - 1) / pps);
-      for (int split = 0; split < n_units; ++split) {
-        const int n = std::max(0, std::min(pages[b], (split + 1) * pps) - split * pps);
-        MinHeap& h = free_at[((int64_t)b * ms + split) & 7];
-        for (int r = 0; r < n_rg; ++r) {
-          const int64_t t = h.top() + kFixedPages + n;
-          h.pop();
-          h.push(t);
-          end = std::max(end, t);
-        }
-      }
+    const int64_t grid = mla::decode_grid_size(B, ms, n_rg);
+    for (int64_t i = 0; i < grid; ++i) {
+      const int64_t u = mla::decode_item(i, B, ms, n_rg) / n_rg;
+      if (u >= (int64_t)B * ms) continue;
+      const int split = (int)(u / B), b = (int)(u - (int64_t)split * B);
+      const int n = std::max(0, std::min(pages[b], (split + 1) * pps) - split * pps);
+      if (n == 0 && !(split == 0 && pages[b] == 0)) continue;
+      MinHeap& h = free_at[i & 7];
+      const int64_t t = h.top() + kFixedPages + n;
+      h.pop();
+      h.push(t);
+      end = std::max(end, t);
     }
     return end;
   };

@@ -51,27 +51,14 @@ struct SwzBf16 {
   }
 };
 
-// Workgroup -> (request, split, row group).  The hardware hands workgroup i
-// to XCD i % 8, in order of i.  Items v = (split * B + b) * n_rg + rg run in
-// split-major order, and within every block of 64 workgroups the 8 x 8
-// (workgroup, XCD) grid is transposed, so items 8c .. 8c+7 all go to XCD c % 8
-// and start together.  Eight consecutive items are then the row groups of a
-// unit and the same split of neighbouring requests: when requests that share
-// a prefix are adjacent in the batch (the page map of each names the same
-// physical pages), their workgroups read each shared page at about the same
-// time on one XCD, and its L2 serves all but the first read.  Each XCD gets
-// an equal share of the items; a last block of fewer than 64 workgroups, and
-// a batch of one request, go round robin.  Grid size:
-// decode_grid_size(B, max_splits, n_rg).
+// Workgroup -> (request, split, row group) through decode_item (launch.h).
+// Grid size: decode_grid_size(B, max_splits, n_rg).
 struct WorkUnit {
   int b, split, rg;
   bool valid;
 };
 __device__ __forceinline__ WorkUnit decode_work_unit(int B, int max_splits, int n_rg) {
-  const int id = blockIdx.x;
-  const int grid = (int)decode_grid_size(B, max_splits, n_rg);
-  const int full = B > 1 ? grid & ~63 : 0;  // one request shares no pages: round robin throughout
-  const int v = id < full ? (id & ~63) | ((id & 7) << 3) | ((id >> 3) & 7) : id;
+  const int v = (int)decode_item(blockIdx.x, B, max_splits, n_rg);
   const int u = v / n_rg;
   WorkUnit w;
   w.rg = v - u * n_rg;

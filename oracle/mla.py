@@ -103,24 +103,27 @@ def attend(Q: np.ndarray, K: np.ndarray, visible: np.ndarray, softmax_scale: flo
 
 
 def decode_ref(q_bits, cache, scales, block_table, seq_lens, *, n_q, H, cache_dtype,
-               scale_mode, softmax_scale, tensor_scale=None, requests=None):
+               scale_mode, softmax_scale, tensor_scale=None, requests=None, queries=None):
     """The attention the decode path computes, request by request.
 
-    q_bits: bf16 bits [B, n_q, H, 576].  Returns (out fp64 [B, n_q, H, 512],
-    lse fp64 [B, n_q, H]); requests not listed in ``requests`` stay zero / NaN.
+    q_bits: bf16 bits [B, n_q, H, 576].  Query i of request b is position
+    L_b - n_q + i and sees tokens t < L_b - n_q + i + 1.  Returns (out fp64
+    [B, n_q, H, 512], lse fp64 [B, n_q, H]); requests not listed in
+    ``requests``, and queries not listed in ``queries``, stay zero / NaN.
     """
     B = int(q_bits.shape[0])
     out = np.zeros((B, n_q, H, DV), dtype=np.float64)
     lse = np.full((B, n_q, H), np.nan, dtype=np.float64)
     todo = range(B) if requests is None else requests
+    qs = np.arange(n_q) if queries is None else np.asarray(queries, dtype=np.int64)
     for b in todo:
         L = int(seq_lens[b])
         K = request_rows(cache, scales, block_table, b, L, cache_dtype, scale_mode, tensor_scale)
-        Q = bf16_to_f64(q_bits[b]).reshape(n_q * H, D)
-        visible = np.repeat(L - n_q + np.arange(n_q) + 1, H)
+        Q = bf16_to_f64(q_bits[b][qs]).reshape(qs.size * H, D)
+        visible = np.repeat(L - n_q + qs + 1, H)
         o, l = attend(Q, K, visible, softmax_scale)
-        out[b] = o.reshape(n_q, H, DV)
-        lse[b] = l.reshape(n_q, H)
+        out[b, qs] = o.reshape(qs.size, H, DV)
+        lse[b, qs] = l.reshape(qs.size, H)
     return out, lse
 
 

@@ -16,4 +16,5 @@ from .workloads import (  # noqa: F401
     custom,
     make,
     CONFIG_NAMES,
+    EXTEND_NAMES,
 )

@@ -315,6 +315,11 @@ CONFIG_NAMES = (
     "bf16_pool_b32",
     "fp8_spec4_b16",
 )
+# extend / prefill: a chunk of new tokens, causal among themselves, over a cached context
+EXTEND_NAMES = (
+    "bf16_extend_16k",
+    "fp8_extend_16k",
+)
 
 
 def make(name: str, seed: int = 0) -> Workload:
@@ -335,6 +340,11 @@ def make(name: str, seed: int = 0) -> Workload:
       cache (the capacity comparison).
     * ``fp8_spec4_b16``: 16 requests, 4 causal query tokens each, 142,000
       cached tokens (+4 appended), per-token scales.
+    * ``bf16_extend_16k``: 1 request, 64 heads, 512 new tokens (queries,
+      causal among themselves) at the end of 16,896 tokens in a bf16 cache
+      (the new rows already in it), randomly permuted pages.
+    * ``fp8_extend_16k``: the same shape on an e4m3 cache with per-token
+      scales, the 512 new rows appended by the step.
     """
     rs = _rng(seed, 0)
     if name == "tiny_bf16":
@@ -358,7 +368,12 @@ def make(name: str, seed: int = 0) -> Workload:
     elif name == "fp8_spec4_b16":
         w = custom(name, B=16, n_q=4, H=64, context_lens=(142_000,) * 16, cache_dtype="fp8",
                    scale_mode="token", seed=seed)
+    elif name == "bf16_extend_16k":
+        w = custom(name, B=1, n_q=512, H=64, context_lens=(16_896,), cache_dtype="bf16", seed=seed)
+    elif name == "fp8_extend_16k":
+        w = custom(name, B=1, n_q=512, H=64, context_lens=(16_384,), cache_dtype="fp8",
+                   scale_mode="token", seed=seed)
     else:
-        raise KeyError(f"unknown workload {name!r}; known: {CONFIG_NAMES}")
+        raise KeyError(f"unknown workload {name!r}; known: {CONFIG_NAMES + EXTEND_NAMES}")
     w.name = name
     return w

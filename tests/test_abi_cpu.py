@@ -58,7 +58,7 @@ def test_decode_argument_validation(lib):
     assert _decode(lib, ms=4, op=None, lp=None) == 1
     assert _decode(lib, H=0) == 2
     assert _decode(lib, H=129) == 2
-    assert _decode(lib, n_q=9) == 2
+    assert _decode(lib, n_q=2049) == 2
     assert _decode(lib, n_q=0) == 2
     assert _decode(lib, pps=0) == 2
     assert _decode(lib, ms=0) == 2
@@ -124,7 +124,7 @@ def test_append_and_combine_validation(lib):
     assert lib.kv_append_fp8(None, None, None, 2, None, None, 0, 4, 1, 1, None) == 0
     assert lib.mla_decode_combine(None, P(1), P(1), 1, 1, 1, 1, 1, 2, P(1), P(1), None, None) == 1
     assert lib.mla_decode_combine(P(1), P(1), P(1), 1, 1, 1, 1, 0, 2, P(1), P(1), None, None) == 2
-    assert lib.mla_decode_combine(P(1), P(1), P(1), 1, 9, 1, 1, 1, 2, P(1), P(1), None, None) == 2
+    assert lib.mla_decode_combine(P(1), P(1), P(1), 1, 2049, 1, 1, 1, 2, P(1), P(1), None, None) == 2
     assert lib.mla_status_string(3) == b"unsupported configuration"
 
 
@@ -230,10 +230,11 @@ def test_plan_rejects_bad_input():
 
 
 def _model_makespan(lens, n_q, H, pps, cus, fixed=2, rows=64):
-    """The planner's duration model written out: workgroups in 1-D launch order
-    (units b * max_splits + split round robin over 8 XCDs, row groups
-    consecutive), workgroup i on the first free compute unit of XCD i % 8,
-    costing a fixed start plus its pages."""
+    """The planner's duration model written out: workgroup i in 1-D launch order
+    on the first free compute unit of XCD i % 8, costing a fixed start plus its
+    pages, working on item v = (split * B + b) * n_rg + rg, where v is i with
+    its two low octal digits swapped inside every full block of 64 (unless the
+    batch is one request of one row group), i itself otherwise."""
     import heapq
 
     pages = [-(-int(L) // 64) for L in lens]
@@ -243,11 +244,13 @@ def _model_makespan(lens, n_q, H, pps, cus, fixed=2, rows=64):
     grid = (B * ms + 7) // 8 * 8 * n_rg
     pools = [[0] * max(1, cus // 8) for _ in range(8)]
     end = 0
+    full = grid // 64 * 64 if (B > 1 or n_rg > 1) else 0
     for i in range(grid):
-        u = (i >> 3) // n_rg * 8 + (i & 7)
+        v = (i // 64) * 64 + (i % 8) * 8 + (i // 8) % 8 if i < full else i
+        u = v // n_rg
         if u >= B * ms:
             continue
-        b, s = divmod(u, ms)
+        s, b = divmod(u, B)
         n = min(pages[b], s * pps + pps) - s * pps
         if n <= 0 and s != 0:
             continue

@@ -41,6 +41,10 @@ CASES = [
     dict(name="bf16_h128", B=2, n_q=1, H=128, context_lens=(640, 77), cache_dtype="bf16"),
     dict(name="bf16_nq5_h64", B=1, n_q=5, H=64, context_lens=(333,), cache_dtype="bf16"),
     dict(name="bf16_nq8_h128", B=1, n_q=8, H=128, context_lens=(256,), cache_dtype="bf16"),
+    # extend / prefill chunks: many new tokens, causal among themselves
+    dict(name="bf16_extend_nq64", B=2, n_q=64, H=16, context_lens=(300, 1000), cache_dtype="bf16"),
+    dict(name="fp8_extend_nq130", B=1, n_q=130, H=16, context_lens=(700,), cache_dtype="fp8",
+         scale_mode="token"),
 ]
 
 

@@ -264,6 +264,28 @@ def test_causal_rows():
     check_causal_rows()
 
 
+def test_query_subset_is_the_causal_prefix():
+    """queries=[...] computes only those queries, each as a single query at
+    length L - n_q + i + 1 (the causal definition, pinned above); the others
+    stay NaN."""
+    rng = np.random.default_rng(19)
+    T, n_q, H = 200, 6, 2
+    rows = _bf16(rng.standard_normal((T, 576)))
+    cache, bt = _paged_bf16(rows)
+    q = _bf16(rng.standard_normal((1, n_q, H, 576)))
+    sel = [0, 3, 5]
+    out, lse = mla.decode_ref(q, cache, None, bt, np.array([T], np.int32), n_q=n_q, H=H,
+                              cache_dtype="bf16", scale_mode="none", softmax_scale=SCALE, queries=sel)
+    for i in range(n_q):
+        if i not in sel:
+            assert np.all(np.isnan(lse[0, i]))
+            continue
+        o1, l1 = mla.decode_ref(q[:, i:i + 1], cache, None, bt, np.array([T - n_q + i + 1], np.int32),
+                                n_q=1, H=H, cache_dtype="bf16", scale_mode="none", softmax_scale=SCALE)
+        assert np.allclose(out[0, i], o1[0, 0], rtol=1e-13, atol=1e-15)
+        assert np.allclose(lse[0, i], l1[0, 0], rtol=1e-13, atol=1e-13)
+
+
 def test_row_with_nothing_visible():
     rng = np.random.default_rng(10)
     Q = rng.standard_normal((2, 576))
