@@ -146,11 +146,16 @@ def cpu_baseline(w, repeats, seconds):
     b = 0
     pages = w.pages_of(b)
     ts = w.tensor_scale() if w.scale_mode == "tensor" else None
-    codes = np.zeros((w.num_pages, 64, 576), np.uint8)
-    scales = np.zeros((w.num_pages, 64), np.float32)
-    c, s = omla.fill_pages_ref(w.page_bits(pages), w.scale_mode, ts)
-    codes[pages], scales[pages] = c, s
-    new = w.new_row_bits()[b:b + 1]
+    if w.cache_dtype == "bf16":
+        codes = np.zeros((w.num_pages, 64, 576), np.uint16)  # bf16 bits, the cache as it is
+        codes[pages] = w.page_bits(pages)
+        scales = None
+    else:
+        codes = np.zeros((w.num_pages, 64, 576), np.uint8)
+        scales = np.zeros((w.num_pages, 64), np.float32)
+        c, s = omla.fill_pages_ref(w.page_bits(pages), w.scale_mode, ts)
+        codes[pages], scales[pages] = c, s
+    new = w.new_row_bits()[b:b + 1] if w.n_new else None
     q = w.q_bits()[b:b + 1]
     bt = w.block_table[b:b + 1]
     sl = w.seq_lens[b:b + 1]
@@ -159,7 +164,8 @@ def cpu_baseline(w, repeats, seconds):
         times = []
         while len(times) < min_runs or sum(times) < budget:
             t0 = time.perf_counter()
-            omla.append_ref(new, codes, scales, bt, sl, w.scale_mode, ts)
+            if new is not None:
+                omla.append_ref(new, codes, scales, bt, sl, w.scale_mode, ts)
             omla.decode_ref(q, codes, scales, bt, sl, n_q=w.n_q, H=w.H, cache_dtype=w.cache_dtype,
                             scale_mode=w.scale_mode, softmax_scale=w.softmax_scale, tensor_scale=ts)
             times.append(time.perf_counter() - t0)
@@ -173,7 +179,8 @@ def cpu_baseline(w, repeats, seconds):
             times1 = run(1, 0.0)  # one run: the 1-thread figure is context only
     tokens = int(w.seq_lens[b])
     out = {"value": tokens / t, "unit": "KV-tokens/s", "cores": int(cores), "kind": "oracle",
-           "sample": f"request 0 of {w.name}: append + all {w.H} heads x {w.n_q} queries x {tokens} tokens, "
+           "sample": f"request 0 of {w.name}: {'append + ' if w.n_new else ''}all {w.H} heads x {w.n_q} queries x "
+                     f"{tokens} tokens, "
                      f"median of {len(times)} runs of {t:.2f} s, {sum(times):.1f} s in all (fp64 numpy)",
            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
     if times1:

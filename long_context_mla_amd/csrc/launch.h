@@ -79,17 +79,20 @@ __host__ __device__ inline int64_t decode_grid_size(int64_t B, int64_t max_split
 }
 
 // The item a decode workgroup works on: item v = (split * B + b) * n_rg + rg
-// (split-major).  The hardware hands workgroup i to XCD i % 8 in order of i;
-// within every full block of 64 workgroups the 8 x 8 (workgroup, XCD) grid is
-// transposed, so items 8c .. 8c+7 go to XCD c % 8 and start together: the row
-// groups of a unit (which read the same pages) and the same split of
-// neighbouring requests (which read the same pages when they share a prefix)
-// share one L2.  A one-request, one-row-group batch shares nothing and goes
-// round robin, as does a last block of fewer than 64 workgroups.
+// (split-major).  The hardware hands workgroup i to XCD i % 8 in order of i.
+// Within full block k of 64 workgroups, XCD x takes the block's 8 consecutive
+// items of chunk (x - k) mod 8, which start together there: the row groups of
+// a unit (which read the same pages) and the same split of neighbouring
+// requests (which read the same pages when they share a prefix) share one L2.
+// The chunk an XCD takes turns with the block, so that requests of unequal
+// length spread over all XCDs.  A one-request, one-row-group batch shares
+// nothing and goes round robin, as does a last block of fewer than 64.
 __host__ __device__ inline int64_t decode_item(int64_t i, int64_t B, int64_t max_splits, int64_t n_rg) {
   const int64_t grid = decode_grid_size(B, max_splits, n_rg);
   const int64_t full = (B > 1 || n_rg > 1) ? grid & ~(int64_t)63 : 0;
-  return i < full ? (i & ~(int64_t)63) | ((i & 7) << 3) | ((i >> 3) & 7) : i;
+  if (i >= full) return i;
+  const int64_t k = i >> 6, x = i & 7, t = (i >> 3) & 7;
+  return (k << 6) | (((x - k) & 7) << 3) | t;
 }
 
 hipError_t launch_kv_append(const AppendArgs& a, int scale_mode, hipStream_t stream);

@@ -5,7 +5,8 @@
 //
 // One workgroup per (request, row, 128-dim chunk), 256 threads: 16 groups of
 // 16 lanes, each lane one 16-byte piece (8 values) of the chunk.  Up to 512
-// splits every lane loads all of its group's partials (splits g, g + 16, ...)
+// splits (the instantiation the launch picks) every lane loads all of its
+// group's partials (splits g, g + 16, ...)
 // at once, together with the split LSEs, before anything depends on them: one
 // memory round trip.  The split weights exp(lse_s - max_s lse_s) go through
 // LDS, each lane sums its splits from registers, and an LDS reduction folds
@@ -16,7 +17,6 @@
 namespace mla {
 
 constexpr int kGroups = 16;                  // split groups per workgroup
-constexpr int kHeldSplits = kGroups * 32;    // splits whose partials lanes hold at once
 constexpr int kWeightChunk = 1024;           // split weights held in LDS at a time (streaming)
 
 // Eight consecutive bf16 partial values (16 bytes) added to acc with weight w (exact widening).
@@ -60,6 +60,11 @@ __device__ __forceinline__ void merge_held(const uint16_t* o_b, int64_t o_stride
   }
 }
 
+// MAXK: the most partial loads a lane holds at once (splits up to 16 * MAXK
+// are held).  The kernel's register count, and so how many workgroups share a
+// compute unit, follows MAXK, so the launch picks the smallest that covers
+// max_splits: a batch of many short merges keeps a full compute unit.
+template <int MAXK>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int chunk = blockIdx.x & 3;
   const int br = blockIdx.x >> 2;  // b * R + r
@@ -80,7 +85,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   // before the length is known: every entry below max_splits lies in the
   // buffer, and the ones past the request's splits are masked once the length
   // arrives.
-  const bool held = a.max_splits <= kHeldSplits;
+  const bool held = a.max_splits <= kGroups * MAXK;
   float ls0 = -INFINITY, ls1 = -INFINITY;
   if (held && t < a.max_splits) ls0 = lse_b[(int64_t)t * a.R];
   if (held && t + 256 < a.max_splits) ls1 = lse_b[(int64_t)(t + 256) * a.R];
@@ -100,12 +105,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     if (t >= n_b) ls0 = -INFINITY;
     if (t + 256 >= n_b) ls1 = -INFINITY;
     const int n_k = (n_b + kGroups - 1) / kGroups;
-    if (n_k > 16)
-      merge_held<32>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
-    else if (n_k > 8)
-      merge_held<16>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
-    else if (n_k > 4)
-      merge_held<8>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
+    if (MAXK >= 32 && n_k > 16)
+      merge_held<(MAXK >= 32 ? 32 : 1)>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
+    else if (MAXK >= 16 && n_k > 8)
+      merge_held<(MAXK >= 16 ? 16 : 1)>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
+    else if (MAXK >= 8 && n_k > 4)
+      merge_held<(MAXK >= 8 ? 8 : 1)>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
     else if (n_k > 2)
       merge_held<4>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
     else if (n_k > 1)
@@ -170,7 +175,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const dim3 grid(a.B * a.R * 4), block(256);
-  hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, a);
+  if (a.max_splits <= kGroups * 4)
+    hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, stream, a);
+  else if (a.max_splits <= kGroups * 8)
+    hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, stream, a);
+  else if (a.max_splits <= kGroups * 16)
+    hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<32>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -111,6 +111,31 @@ def test_binding_checks_alignment():
         mla.mla_decode_paged(q, cache, torch.ones(1), "tensor", bt, sl, 0.07, 4, 1, out=out, lse=lse)
 
 
+def test_item_order_is_a_balanced_bijection():
+    """The decode item order (written out as the model above) covers every
+    workgroup once, keeps eight consecutive items on one XCD, and spreads the
+    requests of the 64-request pool over the XCDs within a few per cent."""
+    import numpy as np
+
+    lens = _lens("lognormal64")
+    pages = [-(-int(L) // 64) for L in lens]
+    for B, S, n in [(64, 40, 1), (32, 43, 1), (16, 4, 4), (1, 224, 1), (1, 1, 1024), (3, 5, 2)]:
+        grid = (B * S + 7) // 8 * 8 * n
+        full = grid // 64 * 64 if (B > 1 or n > 1) else 0
+        items = [(i // 64) * 64 + ((i % 8 - i // 64) % 8) * 8 + (i // 8) % 8 if i < full else i
+                 for i in range(grid)]
+        assert sorted(items) == list(range(grid))
+        for i in range(full):
+            assert items[i] // 8 == items[i - i % 64 + (i % 8)] // 8  # same XCD, same chunk
+    B, S, pps = 64, 40, 30
+    load = np.zeros(8)
+    for i in range(B * S):
+        v = (i // 64) * 64 + ((i % 8 - i // 64) % 8) * 8 + (i // 8) % 8
+        s, b = divmod(v, B)
+        load[i % 8] += max(0, min(pages[b], (s + 1) * pps) - s * pps)
+    assert load.max() / load.mean() < 1.1
+
+
 def test_combine_rejects_split_overflow(lib):
     P = ctypes.c_void_p
     assert lib.mla_decode_combine(P(1), P(1), P(1), 1, 1, 1, 1, 2**16, 2**15, P(1), P(1), None, None) == 2
@@ -232,9 +257,10 @@ def test_plan_rejects_bad_input():
 def _model_makespan(lens, n_q, H, pps, cus, fixed=2, rows=64):
     """The planner's duration model written out: workgroup i in 1-D launch order
     on the first free compute unit of XCD i % 8, costing a fixed start plus its
-    pages, working on item v = (split * B + b) * n_rg + rg, where v is i with
-    its two low octal digits swapped inside every full block of 64 (unless the
-    batch is one request of one row group), i itself otherwise."""
+    pages, working on item v = (split * B + b) * n_rg + rg: inside full block k
+    of 64 workgroups (unless the batch is one request of one row group), XCD x
+    takes the block's eight items of chunk (x - k) mod 8 in order; i itself
+    otherwise."""
     import heapq
 
     pages = [-(-int(L) // 64) for L in lens]
@@ -246,7 +272,7 @@ def _model_makespan(lens, n_q, H, pps, cus, fixed=2, rows=64):
     end = 0
     full = grid // 64 * 64 if (B > 1 or n_rg > 1) else 0
     for i in range(grid):
-        v = (i // 64) * 64 + (i % 8) * 8 + (i // 8) % 8 if i < full else i
+        v = (i // 64) * 64 + ((i % 8 - i // 64) % 8) * 8 + (i // 8) % 8 if i < full else i
         u = v // n_rg
         if u >= B * ms:
             continue
