@@ -642,7 +642,12 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
       // the matrix core still works through the queued MFMAs.
       if (it + 2 < n_it) dma_parts(it + 2, 0, 3);
       phase_fence();
+      // P V is the longer chain of the interval (the score waves' softmax
+      // leaves them slack): its MFMAs go first when both waves of a SIMD
+      // have one ready
+      __builtin_amdgcn_s_setprio(1);
       if (!scan) pv(it - 1);
+      __builtin_amdgcn_s_setprio(0);
       phase_fence();
       if (it + 2 < n_it) dma_parts(it + 2, 3, 10);
       settle(fo);
