@@ -362,6 +362,31 @@ __device__ __forceinline__ void mfma32_first_w(f32x16& c, bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void mfma32_drain(f32x16& c0, f32x16& c1, bf16x8 a) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c0), "+v"(c1) : "v"(a));
 }
+// Eight 32 x 32 accumulators ([2][4]) as one operand list: defined afresh by
+// MFMAs on zero operands (the statement waits out their latency), tied to the
+// last operands of a group of hand-placed MFMAs, or fenced before VALU reads.
+#define MLA_O8_DEF(o) "=&v"(o[0][0]), "=&v"(o[0][1]), "=&v"(o[0][2]), "=&v"(o[0][3]), "=&v"(o[1][0]), \
+    "=&v"(o[1][1]), "=&v"(o[1][2]), "=&v"(o[1][3])
+#define MLA_O8(o) "+v"(o[0][0]), "+v"(o[0][1]), "+v"(o[0][2]), "+v"(o[0][3]), "+v"(o[1][0]), "+v"(o[1][1]), \
+    "+v"(o[1][2]), "+v"(o[1][3])
+__device__ __forceinline__ void mfma32_def_zero8(f32x16 (&o)[2][4]) {
+  const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %8, %8, 0\n\tv_mfma_f32_32x32x16_bf16 %1, %8, %8, 0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %2, %8, %8, 0\n\tv_mfma_f32_32x32x16_bf16 %3, %8, %8, 0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %4, %8, %8, 0\n\tv_mfma_f32_32x32x16_bf16 %5, %8, %8, 0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %6, %8, %8, 0\n\tv_mfma_f32_32x32x16_bf16 %7, %8, %8, 0\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : MLA_O8_DEF(o)
+      : "v"(z));
+}
+__device__ __forceinline__ void mfma32_tie8(f32x16 (&o)[2][4], bf16x8 a, bf16x8 b0, bf16x8 b1) {
+  asm volatile("" : MLA_O8(o) : "v"(a), "v"(b0), "v"(b1));
+}
+__device__ __forceinline__ void mfma32_result_fence8(f32x16 (&o)[2][4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : MLA_O8(o));
+}
 __device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

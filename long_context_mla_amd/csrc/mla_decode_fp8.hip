@@ -77,18 +77,29 @@ constexpr int kQLoads = 18;                         // 1 KB query copies per sco
 static_assert(kLdsBytes <= 163840, "LDS");
 static_assert(4 * kRows8 * 272 <= kOffP, "the output tiles fit over the page buffers");
 
-// Staged page layout.  Token t = 16q + m (quarter q, m < 16), 16-byte chunk c
-// of its 576-byte row (36 per row): chunks c < 32 (the V part) sit in V-buffer
-// slot q*512 + (c/4)*64 + 4m + ((c%4) ^ F), chunks 32..35 in rope-buffer slot
-// q*64 + 4m + ((c%4) ^ F), with F = (m/4) ^ (2 (q%2)).  Then
-//  * one LDS-DMA instruction fills one group of 64 slots: lane l brings token
-//    16q + l/4, chunk 4i + ((l%4) ^ F) (one source offset per lane for all
-//    nine groups of its quarter);
-//  * the QK^T operand reads (16 tokens x one 16-byte chunk each 16 lanes)
-//    and the transposing P V reads (8-byte halves of one chunk of tokens
-//    4g..4g+3 and 16+4g..16+4g+3 of a 32-token block, 32 lanes per access)
-//    hit distinct banks.
-__device__ __forceinline__ int swz(int m4, int q) { return m4 ^ ((q & 1) << 1); }
+// Staged page layout.  Token t = 16q + m of the page (quarter q, m < 16).
+// The V part of its row (16-byte chunks c < 32) sits in V-buffer slot
+//   vslot(q, m, c) = q*512 + (c/8)*128 + 8m + ((c%8) ^ vswz(m)),  vswz(m) = (m/2) % 8:
+// eight chunks of one token side by side (128 bytes).  The rope part (chunks
+// 32..35, c' = c - 32) sits in rope-buffer slot
+//   rslot(q, m, c') = q*64 + 8(m/2) + ((4(m%2) + c') ^ rswz(m)),  rswz(m) = (m/4) % 4:
+// two tokens per 128 bytes.  Then
+//  * one LDS-DMA instruction fills one group of 64 slots.  V group i of a
+//    quarter holds tokens 8(i%2) .. +7 and chunks 8(i/2) .. +7 (lane l brings
+//    token 8(i%2) + l/8, chunk 8(i/2) + ((l%8) ^ vswz)); the rope group holds
+//    the quarter's 16 tokens (lane l brings token 2(l/8) + (l/4)%2, rope chunk
+//    (l%4) ^ rswz).  Eight (four) consecutive lanes read one token's bytes.
+//  * the QK^T operand reads (16 tokens of a quarter, one 16-byte chunk each,
+//    per 16 lanes) and the transposing P V reads (8-byte halves of one chunk
+//    of tokens 4g..4g+3 and 16+4g..16+4g+3 of a 32-token block) run without
+//    LDS bank conflicts.  That was measured with the bank-conflict counter on
+//    this chip: a layout with the four chunks of a 64-byte group side by side
+//    (tokens 64 bytes apart) cost four stall cycles on every QK^T read, and
+//    swizzles of two bits instead of three cost as much.
+__device__ __forceinline__ int vswz(int m) { return (m >> 1) & 7; }
+__device__ __forceinline__ int rswz(int m) { return (m >> 2) & 3; }
+__device__ __forceinline__ int vslot(int q, int m, int c) { return q * 512 + (c >> 3) * 128 + 8 * m + ((c & 7) ^ vswz(m)); }
+__device__ __forceinline__ int rslot(int q, int m, int c) { return q * 64 + 8 * (m >> 1) + ((4 * (m & 1) + c) ^ rswz(m)); }
 
 // Keeps the compiler from moving memory accesses across this point (no
 // instruction): it stops loads of a later phase from being hoisted over the
@@ -246,16 +257,14 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     const int lim = r0 + lr < a.R ? L - a.n_q + (r0 + lr) / a.H + 1 : 0;
     const int lim_lo = L - a.n_q + r0 / a.H + 1;
     // LDS byte offsets of this lane's K chunk 2p + sg (token 32th + sn: quarter
-    // tq, token tm of it) within a V buffer (p < 16, plus (p / 2) KB) and a rope
-    // buffer (p = 16, 17), for even and odd p
+    // tq, token tm of it): within a V buffer for p < 16 (kvl[p % 4], plus
+    // (p / 4) * 2 KB) and within a rope buffer for p = 16, 17 (krl[p - 16])
     const int tq = 2 * th + (sn >> 4), tm = sn & 15;
-    uint32_t kvl[2], krl[2];
+    uint32_t kvl[4], krl[2];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int x = (4 * tm + ((2 * e + sg) ^ swz(tm >> 2, tq))) * 16;
-      kvl[e] = (uint32_t)(tq * 8192 + x);
-      krl[e] = (uint32_t)(tq * 1024 + x);
-    }
+    for (int a4 = 0; a4 < 4; ++a4) kvl[a4] = (uint32_t)(vslot(tq, tm, 2 * a4 + sg) * 16);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) krl[e] = (uint32_t)(rslot(tq, tm, 2 * e + sg) * 16);
     float m0 = -INFINITY;    // log2-domain reference of this lane's row
     float ymax = -INFINITY;  // running max of score - reference
     float lsum = 0.0f;       // this lane's share of the softmax sum (fp32 P)
@@ -264,7 +273,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     constexpr int KW = 9;        // K chunks held in registers at a time
     u32x4 kraw[KW];              // chunk p of the page in kraw[p % KW]
     auto k_read = [&](int it, int p) {
-      kraw[p % KW] = p < 16 ? *reinterpret_cast<const u32x4*>(s_v + (it % kVBuf) * kVBytes + kvl[p & 1] + (p >> 1) * 1024)
+      kraw[p % KW] = p < 16 ? *reinterpret_cast<const u32x4*>(s_v + (it % kVBuf) * kVBytes + kvl[p & 3] + (p >> 2) * 2048)
                             : *reinterpret_cast<const u32x4*>(s_rope + (it % kRBuf) * kRBytes + krl[p & 1]);
     };
     f32x16 S;  // S^T tile: element r is token 32th + 8(r/4) + 4sg + r%4 of the lane's row
@@ -457,8 +466,15 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     const int32_t* src = a.block_table + bt_row + min(p_begin + (chunk << 6) + lane, p_end - 1);
     asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(ids) : "v"(src) : "memory");
   };
-  // lane l copies token 16j + l/4, chunk 4i + ((l%4) ^ F) of group i
-  const uint32_t goff = (uint32_t)((16 * j + (lane >> 2)) * 576 + (((lane & 3) ^ swz(lane >> 4, j)) << 4));
+  // Source offsets (within a page) of this lane's 16 bytes of quarter j: V
+  // groups i even and odd (plus 128 (i / 2) bytes), and the rope group.
+  uint32_t goff[3];
+  {
+    const int t8 = lane >> 3, mr = 2 * t8 + ((lane >> 2) & 1);
+    goff[0] = (uint32_t)((16 * j + t8) * kD + 16 * ((lane & 7) ^ vswz(t8)));
+    goff[1] = (uint32_t)((16 * j + 8 + t8) * kD + 16 * ((lane & 7) ^ vswz(8 + t8)));
+    goff[2] = (uint32_t)((16 * j + mr) * kD + 512 + 16 * ((lane & 3) ^ rswz(mr)));
+  }
   // Pieces p0 .. p1-1 of the copy of page it: groups 0..7 of the V part, the
   // rope part, then (per-token scales) the scales.
   auto dma_parts = [&](int it, int p0, int p1) {
@@ -468,8 +484,8 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     const uint32_t vdst = lds_addr(s_v + (it % kVBuf) * kVBytes + j * 8192);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (i >= p0 && i < p1) lds_dma16(src + 64 * i, goff, vdst + 1024 * i);
-    if (8 >= p0 && 8 < p1) lds_dma16(src + 64 * 8, goff, lds_addr(s_rope + (it % kRBuf) * kRBytes + j * 1024));
+      if (i >= p0 && i < p1) lds_dma16(src + 128 * (i >> 1), goff[i & 1], vdst + 1024 * i);
+    if (8 >= p0 && 8 < p1) lds_dma16(src, goff[2], lds_addr(s_rope + (it % kRBuf) * kRBytes + j * 1024));
     // the scales of this wave's own 16 tokens: a row appended in this launch
     // overwrites its scale in LDS after this wave's wait
     if (9 >= p0 && 9 < p1 && SCALE == kScaleToken && lane < 16)
@@ -491,14 +507,13 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
       const float sc = encode_row_e4m3<SCALE == kScaleToken>(
           a.kv_new + ((int64_t)b * a.n_new + (pos - first_new)) * kD, lane, tscale, codes);
       const int t = pos & (kPage - 1), tm = t & 15;
-      const int f = swz(tm >> 2, j);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int c8 = lane + 64 * c;  // 8-byte chunk of the row
         if (c == 0 || lane < 8) {
           const int c16 = c8 >> 1;
-          uint8_t* dst = c16 < 32 ? s_v + (it % kVBuf) * kVBytes + (j * 512 + (c16 >> 2) * 64 + 4 * tm + ((c16 & 3) ^ f)) * 16
-                                  : s_rope + (it % kRBuf) * kRBytes + (j * 64 + 4 * tm + ((c16 & 3) ^ f)) * 16;
+          uint8_t* dst = c16 < 32 ? s_v + (it % kVBuf) * kVBytes + vslot(j, tm, c16) * 16
+                                  : s_rope + (it % kRBuf) * kRBytes + rslot(j, tm, c16 - 32) * 16;
           *reinterpret_cast<u32x2*>(dst + 8 * (c8 & 1)) = codes[c];
         }
       }
@@ -533,11 +548,11 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     const int nvalid = L - (p_begin + it) * kPage;
     if (nvalid < 16 * j + 16) {
       const int tl0 = max(nvalid - 16 * j, 0);
-      const int per = (16 - tl0) * 4;  // slots per group
-      u32x4* v = reinterpret_cast<u32x4*>(s_v + (it % kVBuf) * kVBytes) + j * 512 + tl0 * 4;
-      for (int e = lane; e < 8 * per; e += 64) {
+      const int per = (16 - tl0) * 8;  // slots per group of eight chunks
+      u32x4* v = reinterpret_cast<u32x4*>(s_v + (it % kVBuf) * kVBytes) + j * 512 + tl0 * 8;
+      for (int e = lane; e < 4 * per; e += 64) {
         const int grp = e / per;
-        v[grp * 64 + (e - grp * per)] = u32x4{0u, 0u, 0u, 0u};
+        v[grp * 128 + (e - grp * per)] = u32x4{0u, 0u, 0u, 0u};
       }
     }
     if (a.n_new > 0) patch_new_rows(it);
@@ -554,14 +569,13 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   // 8h .. 8h+7 of 16-byte chunk 8j + db: token 32kb + 16(g/2) + mm with
   // mm = 4(g%2) + jj + 4(jj/4), the order the score waves write P in (their
   // S^T tiles hold tokens 8r' + 4sg + i).  Within quarter 2kb + g/2 that is
-  // slot (2j + db/4)*64 + 4mm + ((db%4) ^ F), F = (mm/4) ^ 2(g/2).
-  uint32_t voff[4];
+  // vslot(2kb + g/2, mm, 8j + db): voff[db] plus kb * 16 KB and j * 2 KB.
+  uint32_t voff[8];
   {
     const int jj = m >> 1, h = m & 1, hq = g >> 1;
     const int mm = 4 * (g & 1) + jj + 4 * (jj >> 2);
-    const int f = (mm >> 2) ^ (hq << 1);
 #pragma unroll
-    for (int d3 = 0; d3 < 4; ++d3) voff[d3] = (uint32_t)((hq * 512 + 4 * mm + (d3 ^ f)) * 16 + 8 * h);
+    for (int db = 0; db < 8; ++db) voff[db] = (uint32_t)(vslot(hq, mm, db) * 16 + 8 * h);
   }
   const uint32_t poff = (uint32_t)(m * 128);  // + row block, chunk (kb, g) ^ (m >> 1)
   auto pv = [&](int it) {
@@ -576,7 +590,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
         pop[rb] = *reinterpret_cast<const bf16x8*>(pp + poff + rb * 2048 + (((4 * kb + g) ^ ((m >> 1) & 7)) << 4));
 #pragma unroll
       for (int db = 0; db < 8; ++db)
-        vraw[db] = lds_read_tr8(vb + voff[db & 3] + kb * 16384 + (2 * j + (db >> 2)) * 1024);
+        vraw[db] = lds_read_tr8(vb + voff[db] + kb * 16384 + j * 2048);
       uint32_t d[2][4];
       d[0][0] = cvt_e4m3_lo(vraw[0].x);
       d[0][1] = cvt_e4m3_hi(vraw[0].x);
