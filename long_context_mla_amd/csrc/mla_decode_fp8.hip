@@ -616,20 +616,21 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     }
   };
 
-  // pages 0 and 1 go out before the query barrier (their buffers are not the
-  // query's); a rerun sends them again at the end of its first pass
-  auto first_pages = [&]() {
-    dma_page(0);
-    if (n_it > 1) dma_page(1);
-  };
+  // Page 0 goes out before the query barrier (its buffers are not the
+  // query's), page 1 only once page 0 has landed: at the start every compute
+  // unit asks for its first pages at once, and page 0 alone lands sooner
+  // (measured 0.3-0.6 us per launch) than pages 0 and 1 together.  A rerun
+  // sends page 0 again at the end of its first pass.
+  auto first_pages = [&]() { dma_page(0); };
   first_pages();
   __syncthreads();  // (Q)
   for (;;) {
     bool scan = false;
     mfma_def_zero_o(Oa);
     mfma_def_zero_o(Ob);
-    // page 0 landed
-    if (n_it > 1) wait_vmcnt<LPP>(); else wait_vmcnt<0>();
+    // page 0 landed; page 1 goes out
+    wait_vmcnt<0>();
+    if (n_it > 1) dma_page(1);
     staged(0);
     __syncthreads();  // (A)
     if (!have_ref) {
