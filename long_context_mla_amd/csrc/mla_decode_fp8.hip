@@ -20,7 +20,9 @@
 //    P V over the previous page, V being the first 512 columns of the same
 //    staged rows (transposing LDS reads), and copies quarter j (tokens
 //    16j .. 16j+15) of every page HBM -> LDS by LDS-DMA, two pages ahead.
-// One barrier per page separates "scores of page p" from "P V of page p".
+// Two barriers per page: D separates "scores of page p" from "P V of page p",
+// and M, once the score waves have issued QK^T of page p + 1, starts P V of
+// page p, so that it runs beside their softmax.
 //
 // LDS: the V parts (first 512 bytes of each row) of four pages, the rope parts
 // (last 64 bytes) of three (rope bytes are dead once the scores of their page
@@ -90,8 +92,8 @@ static_assert(4 * kRows8 * 272 <= kOffP, "the output tiles fit over the page buf
 //    the quarter's 16 tokens (lane l brings token 2(l/8) + (l/4)%2, rope chunk
 //    (l%4) ^ rswz).  Eight (four) consecutive lanes read one token's bytes.
 //  * the QK^T operand reads (16 tokens of a quarter, one 16-byte chunk each,
-//    per 16 lanes) and the transposing P V reads (8-byte halves of one chunk
-//    of tokens 4g..4g+3 and 16+4g..16+4g+3 of a 32-token block) run without
+//    per 16 lanes) and the transposing P V reads (8-byte halves of chunks x
+//    and x ^ 2 of tokens 4u..4u+3 and 8+4u..8+4u+3 of a quarter) run without
 //    LDS bank conflicts.  That was measured with the bank-conflict counter on
 //    this chip: a layout with the four chunks of a 64-byte group side by side
 //    (tokens 64 bytes apart) cost four stall cycles on every QK^T read, and
@@ -408,6 +410,9 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
             settle(fw);
             if (allow_scan && fw != 0u) scan = true;
           }
+          // (M) QK^T of page it is issued: the output waves start P V of
+          // page it - 1, which then runs beside this wave's softmax
+          if (p == KP - 1) __syncthreads();
         });
         scores(it);
         if (!scan) weights(it);
@@ -558,62 +563,81 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     if (a.n_new > 0) patch_new_rows(it);
   };
 
-  // O^T = V^T P^T on the matrix core, so that lane (m, g) of [rb][db] holds
-  // dims 128j + 16db + 4g + i (i < 4) of row 16rb + m: four consecutive output
-  // values of one row, stored straight from registers at the end.  Row blocks
-  // 0, 1 in Oa, 2, 3 in Ob (two arrays, each handed whole to the MFMA fences,
-  // so both stay in VGPRs).
-  f32x4 Oa[2][8], Ob[2][8];
-  // Per-lane LDS offsets of the V reads.  Lane 2jj + h of 16-lane group g
-  // addresses the token of k index 8g + jj of the 32-token block kb, bytes
-  // 8h .. 8h+7 of 16-byte chunk 8j + db: token 32kb + 16(g/2) + mm with
-  // mm = 4(g%2) + jj + 4(jj/4), the order the score waves write P in (their
-  // S^T tiles hold tokens 8r' + 4sg + i).  Within quarter 2kb + g/2 that is
-  // vslot(2kb + g/2, mm, 8j + db): voff[db] plus kb * 16 KB and j * 2 KB.
-  uint32_t voff[8];
+  // O^T = V^T P^T on v_mfma_f32_32x32x16_bf16.  O[rt][dt] is the 32 x 32
+  // tile of rows 32rt .. 32rt+31 and of the 32 dims of chunks ca(dt) and
+  // ca(dt) ^ 2 of this wave's eight 16-dim chunks, ca(dt) = dt%2 + 4(dt/2)
+  // (that pairing keeps the V reads below free of bank conflicts).  Lane l
+  // holds row 32rt + l%32 and, in element i, tile dim M = 8(i/4) + 4(l/32) + i%4:
+  // dim M%16 of chunk ca(dt) ^ 2(M/16).  A page is four k-steps of 16 tokens,
+  // k-step s being quarter s of the staged page.  K index 8u + e (u = l/32,
+  // e < 8) of k-step s is token 16s + 4u + e + 4(e/4), the order the score
+  // waves write P in (chunk 2s + u of a row of P holds those eight tokens), so
+  // the P operand of lane l is one 16-byte read.
+  f32x16 O[2][4];
+  // V operand: a transposing read per (k-step, dim tile).  Lane 2e + h of
+  // 16-lane group G addresses k index 8(G/2) + e of the step, i.e. token
+  // m = 4(G/2) + e + 4(e/4) of the quarter, 8-byte half h of chunk
+  // 8j + (ca(dt) ^ 2(G%2)): vslot(s, m, that chunk), i.e. vo[dt] plus
+  // s * 8 KB and j * 2 KB.
+  uint32_t vo[4];
   {
-    const int jj = m >> 1, h = m & 1, hq = g >> 1;
-    const int mm = 4 * (g & 1) + jj + 4 * (jj >> 2);
+    const int e = m >> 1, h = m & 1;
+    const int mt = 4 * (g >> 1) + e + 4 * (e >> 2);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) voff[db] = (uint32_t)(vslot(hq, mm, db) * 16 + 8 * h);
+    for (int dt = 0; dt < 4; ++dt)
+      vo[dt] = (uint32_t)(vslot(0, mt, ((dt & 1) + 4 * (dt >> 1)) ^ (2 * (g & 1))) * 16 + 8 * h);
   }
-  const uint32_t poff = (uint32_t)(m * 128);  // + row block, chunk (kb, g) ^ (m >> 1)
+  // P operand: row 32rt + l%32, chunk 2s + l/32, stored at chunk position
+  // (2s + l/32) ^ ((row / 2) % 8) (the row swizzle does not depend on rt).
+  uint32_t po[4];
+  {
+    const int pr = lane & 31, sw = (pr >> 1) & 7;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) po[st] = (uint32_t)(pr * 128 + (((2 * st + (lane >> 5)) ^ sw) << 4));
+  }
   auto pv = [&](int it) {
     const uint8_t* vb = s_v + (it % kVBuf) * kVBytes;
     const uint8_t* pp = s_p + (it & 1) * kPBytes;
+    u32x2 vr[2][4];    // [step parity][dim tile]: raw fp8 V operands
+    bf16x8 pb[2][2];   // [step parity][row tile]: P operands
+    auto load = [&](int st) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 pop[4];  // [row block]
-      u32x2 vraw[8];  // [16-dim block]
+      for (int dt = 0; dt < 4; ++dt) vr[st & 1][dt] = lds_read_tr8(vb + vo[dt] + st * 8192 + j * 2048);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        pop[rb] = *reinterpret_cast<const bf16x8*>(pp + poff + rb * 2048 + (((4 * kb + g) ^ ((m >> 1) & 7)) << 4));
+      for (int rt = 0; rt < 2; ++rt) pb[st & 1][rt] = *reinterpret_cast<const bf16x8*>(pp + po[st] + rt * 4096);
+    };
+    load(0);
+    uint32_t d[2][4];
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
-        vraw[db] = lds_read_tr8(vb + voff[db] + kb * 16384 + j * 2048);
-      uint32_t d[2][4];
-      d[0][0] = cvt_e4m3_lo(vraw[0].x);
-      d[0][1] = cvt_e4m3_hi(vraw[0].x);
-      d[0][2] = cvt_e4m3_lo(vraw[0].y);
-      d[0][3] = cvt_e4m3_hi(vraw[0].y);
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const bf16x8 vop = bf16x8_of(d[db & 1]);
-        uint32_t (&nx)[4] = d[(db + 1) & 1];
-        const bool more = db + 1 < 8;
-        mfma_vvv_w(Oa[0][db], vop, pop[0]);
-        if (more) nx[0] = cvt_e4m3_lo(vraw[db + 1].x);
-        mfma_vvv(Oa[1][db], vop, pop[1]);
-        if (more) nx[1] = cvt_e4m3_hi(vraw[db + 1].x);
-        mfma_vvv(Ob[0][db], vop, pop[2]);
-        if (more) nx[2] = cvt_e4m3_lo(vraw[db + 1].y);
-        mfma_vvv(Ob[1][db], vop, pop[3]);
-        if (more) nx[3] = cvt_e4m3_hi(vraw[db + 1].y);
-      }
-      mfma_drain_o(Oa, pop[0], pop[1], bf16x8_of(d[1]));
-      mfma_tie_o(Ob, pop[2], pop[3], bf16x8_of(d[1]));
+    for (int st = 0; st < 4; ++st) {
+      // the next step's operands are read while this step's MFMAs run
+      if (st + 1 < 4) load(st + 1);
       phase_fence();
+      const u32x2 (&v)[4] = vr[st & 1];
+      d[0][0] = cvt_e4m3_lo(v[0].x);
+      d[0][1] = cvt_e4m3_hi(v[0].x);
+      d[0][2] = cvt_e4m3_lo(v[0].y);
+      d[0][3] = cvt_e4m3_hi(v[0].y);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const bf16x8 vop = bf16x8_of(d[dt & 1]);
+        uint32_t (&nx)[4] = d[(dt + 1) & 1];
+        const bool more = dt + 1 < 4;
+        mfma32_w(O[0][dt], vop, pb[st & 1][0]);
+        if (more) {
+          nx[0] = cvt_e4m3_lo(v[dt + 1].x);
+          nx[1] = cvt_e4m3_hi(v[dt + 1].x);
+        }
+        mfma32(O[1][dt], vop, pb[st & 1][1]);
+        if (more) {
+          nx[2] = cvt_e4m3_lo(v[dt + 1].y);
+          nx[3] = cvt_e4m3_hi(v[dt + 1].y);
+        }
+      }
     }
+    // the last MFMAs' operands stay held until the next statement
+    mfma32_tie8(O, bf16x8_of(d[1]), pb[1][0], pb[1][1]);
+    phase_fence();
   };
 
   // Page 0 goes out before the query barrier (its buffers are not the
@@ -626,8 +650,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   __syncthreads();  // (Q)
   for (;;) {
     bool scan = false;
-    mfma_def_zero_o(Oa);
-    mfma_def_zero_o(Ob);
+    mfma32_def_zero8(O);
     // page 0 landed; page 1 goes out
     wait_vmcnt<0>();
     if (n_it > 1) dma_page(1);
@@ -650,21 +673,21 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     // page's flags are looked at; a scan then throws it away with the rest.)
     uint32_t fo = flag_word(0);
     for (int it = 1; it <= n_it; ++it) {
-      // The copy of page it + 2: three pieces before P V of page it - 1, the
-      // rest after it is issued (its buffers were last read by P V of page
-      // it - 2 and QK^T of page it - 1, both before barrier D).  A piece that
-      // waits for room in the memory pipeline then holds up the wave while
-      // the matrix core still works through the queued MFMAs.
-      if (it + 2 < n_it) dma_parts(it + 2, 0, 3);
+      // The copy of page it + 2 (its buffers were last read by P V of page
+      // it - 2 and QK^T of page it - 1, both before barrier D), issued while
+      // this wave would wait anyway: P V of page it - 1 starts only at barrier
+      // M, once the score waves have issued QK^T of page it.  QK^T then has
+      // the matrix core to itself, and P V overlaps the score waves' softmax
+      // instead of QK^T (measured 2-3 % per launch over interleaving the two;
+      // neither a barrier with the 16x16x32 P V nor the 32x32x16 P V without
+      // one gained).  The last pass (it = n_it) has no QK^T to wait for.
+      if (it + 2 < n_it) dma_page(it + 2);
+      if (it < n_it) __syncthreads();  // (M)
       phase_fence();
-      // P V is the longer chain of the interval (the score waves' softmax
-      // leaves them slack): its MFMAs go first when both waves of a SIMD
-      // have one ready
       __builtin_amdgcn_s_setprio(1);
       if (!scan) pv(it - 1);
       __builtin_amdgcn_s_setprio(0);
       phase_fence();
-      if (it + 2 < n_it) dma_parts(it + 2, 3, 10);
       settle(fo);
       if (allow_scan && fo != 0u) scan = true;
       if (it == n_it) break;
@@ -683,41 +706,43 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   }
 
   __syncthreads();  // (F) the score waves' sums are in LDS; every page buffer is free
-  // Normalisation: lane (m, g) owns rows 16rb + m; the output is a weighted
+  // Normalisation: lane l owns rows 32rt + l%32; the output is a weighted
   // mean with the bf16 weights P V used, the LSE uses the fp32 weights (lanes
-  // g == 0 of wave 4 write it).
+  // l < 32 of wave 4 write it).
   const bool single = a.max_splits == 1;
   const int64_t prow0 = single ? (int64_t)b * a.R + r0 : ((int64_t)b * a.max_splits + split) * a.R + r0;
-  float inv[4];
+  float inv[2];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int row = 16 * rb + m;
+  for (int rt = 0; rt < 2; ++rt) {
+    const int row = 32 * rt + (lane & 31);
     const float ln = s_lnrm[row] + s_lnrm[64 + row];
-    inv[rb] = ln > 0.0f ? tscale / ln : 0.0f;
-    if (j == 0 && g == 0 && r0 + row < a.R) {
+    inv[rt] = ln > 0.0f ? tscale / ln : 0.0f;
+    if (j == 0 && lane < 32 && r0 + row < a.R) {
       const float lt = s_lsum[row] + s_lsum[64 + row];
       const float mr = s_m0[row] == -INFINITY ? 0.0f : s_m0[row];
       (single ? a.lse : a.lse_part)[prow0 + row] = lt > 0.0f ? (mr + __log2f(lt)) * kLn2 : -INFINITY;
     }
   }
-  // Stores: lane (m, g) holds, per [rb][db], four consecutive bf16 of row
-  // 16rb + m.  They go through LDS (this wave's 64 rows x 256 bytes, rows 272
-  // bytes apart: conflict-free 8-byte writes of this layout and 16-byte reads
-  // of whole rows) so that each store moves 16 contiguous bytes per lane and
-  // 16 lanes fill one row's 256 bytes.  Only this wave touches its tile, and a
-  // wave's LDS accesses complete in order.
-  mfma_result_fence_v16(Oa);
-  mfma_result_fence_v16(Ob);
+  // Stores: lane l holds, per [rt][dt] and k = i/4, four consecutive bf16 of
+  // row 32rt + l%32: dims 8(k%2) + 4(l/32) .. +3 of chunk ca(dt) ^ 2(k/2).  They go through LDS (this wave's 64 rows x 256 bytes, rows
+  // 272 bytes apart: 16-byte reads of whole rows) so that each store moves 16
+  // contiguous bytes per lane and 16 lanes fill one row's 256 bytes.  Only
+  // this wave touches its tile, and a wave's LDS accesses complete in order.
+  mfma32_result_fence8(O);
   constexpr int kTileStride = 272;
   uint8_t* tile = lds + j * (kRows8 * kTileStride);
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const f32x4 o = rb < 2 ? Oa[rb][db] : Ob[rb - 2][db];
-      *reinterpret_cast<u32x2*>(tile + (16 * rb + m) * kTileStride + 32 * db + 8 * g) =
-          u32x2{pack_bf16x2(o[0] * inv[rb], o[1] * inv[rb]), pack_bf16x2(o[2] * inv[rb], o[3] * inv[rb])};
-    }
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x16& o = O[rt][dt];
+        const int ch = ((dt & 1) + 4 * (dt >> 1)) ^ (2 * (k >> 1));
+        *reinterpret_cast<u32x2*>(tile + (32 * rt + (lane & 31)) * kTileStride + 32 * ch + 16 * (k & 1) + 8 * (lane >> 5)) =
+            u32x2{pack_bf16x2(o[4 * k] * inv[rt], o[4 * k + 1] * inv[rt]),
+                  pack_bf16x2(o[4 * k + 2] * inv[rt], o[4 * k + 3] * inv[rt])};
+      }
   uint16_t* dst = (single ? a.out : a.o_part) + prow0 * kDV + j * 128;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
