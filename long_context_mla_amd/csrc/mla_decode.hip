@@ -440,14 +440,14 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
       if (a.max_splits == 1) {
         uint16_t* dst = a.out + ((int64_t)b * a.R + r) * kDV + dim0 + m;
 #pragma unroll
-        for (int db = 0; db < 8; ++db) dst[db * 16] = float_to_bf16(O[rbp][db][i] * inv);
-        if (wave == 0 && m == 0) a.lse[(int64_t)b * a.R + r] = lse_nat;
+        for (int db = 0; db < 8; ++db) __builtin_nontemporal_store(float_to_bf16(O[rbp][db][i] * inv), dst + db * 16);
+        if (wave == 0 && m == 0) __builtin_nontemporal_store(lse_nat, a.lse + (int64_t)b * a.R + r);
       } else {
         const int64_t pr = ((int64_t)b * a.max_splits + split) * a.R + r;
         uint16_t* dst = a.o_part + pr * kDV + dim0 + m;
 #pragma unroll
-        for (int db = 0; db < 8; ++db) dst[db * 16] = float_to_bf16(O[rbp][db][i] * inv);
-        if (wave == 0 && m == 0) a.lse_part[pr] = lse_nat;
+        for (int db = 0; db < 8; ++db) __builtin_nontemporal_store(float_to_bf16(O[rbp][db][i] * inv), dst + db * 16);
+        if (wave == 0 && m == 0) __builtin_nontemporal_store(lse_nat, a.lse_part + pr);
       }
     }
 }

@@ -720,11 +720,15 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
     if (j == 0 && lane < 32 && r0 + row < a.R) {
       const float lt = s_lsum[row] + s_lsum[64 + row];
       const float mr = s_m0[row] == -INFINITY ? 0.0f : s_m0[row];
-      (single ? a.lse : a.lse_part)[prow0 + row] = lt > 0.0f ? (mr + __log2f(lt)) * kLn2 : -INFINITY;
+      __builtin_nontemporal_store(lt > 0.0f ? (mr + __log2f(lt)) * kLn2 : -INFINITY, (single ? a.lse : a.lse_part) + prow0 + row);
     }
   }
   // Stores: lane l holds, per [rt][dt] and k = i/4, four consecutive bf16 of
-  // row 32rt + l%32: dims 8(k%2) + 4(l/32) .. +3 of chunk ca(dt) ^ 2(k/2).  They go through LDS (this wave's 64 rows x 256 bytes, rows
+  // row 32rt + l%32: dims 8(k%2) + 4(l/32) .. +3 of chunk ca(dt) ^ 2(k/2).
+  // The global stores are non-temporal: every workgroup of a launch writes
+  // its 64 KB at about the same time, and with ordinary stores the lines were
+  // still dirty in L2 when the launch ended (measured 1.0 us per launch at
+  // 100k tokens, the combine reading them back 0.5 us slower).  They go through LDS (this wave's 64 rows x 256 bytes, rows
   // 272 bytes apart: 16-byte reads of whole rows) so that each store moves 16
   // contiguous bytes per lane and 16 lanes fill one row's 256 bytes.  Only
   // this wave touches its tile, and a wave's LDS accesses complete in order.
@@ -748,7 +752,7 @@ __global__ __launch_bounds__(512, 1) void decode_fp8_kernel(DecodeArgs a) {
   for (int k = 0; k < 16; ++k) {
     const int row = 4 * k + (lane >> 4), c = lane & 15;  // 64 rows x 16 chunks of 8 dims
     const u32x4 v = *reinterpret_cast<const u32x4*>(tile + row * kTileStride + 16 * c);
-    if (r0 + row < a.R) *reinterpret_cast<u32x4*>(dst + (int64_t)row * kDV + 8 * c) = v;
+    if (r0 + row < a.R) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + (int64_t)row * kDV + 8 * c));
   }
 }
 
