@@ -1,5 +1,5 @@
-// Shared definitions of the decode kernels: the staged page tile, its LDS
-// swizzle, LDS-DMA copies and wait helpers.
+// Shared definitions of the decode kernels: the work-unit decode, LDS-DMA
+// copies and wait helpers.
 #pragma once
 
 #include "device_common.h"
@@ -7,49 +7,7 @@
 
 namespace mla {
 
-constexpr int kRows = 32;           // query rows per workgroup
 constexpr float kRefSlack = 64.0f;  // log2 headroom of the weights over the reference
-constexpr int kMaxRestarts = 4;
-
-template <int CACHE>
-struct Tile {
-  static constexpr int ELEM = CACHE == kFp8 ? 1 : 2;
-  static constexpr int ROW_BYTES = kD * ELEM;
-  static constexpr int PAGE_BYTES = kPage * ROW_BYTES;
-  // FP8 pages are small enough for four LDS buffers, which lets P V of a page
-  // run one iteration after its scores (one barrier per page) with two pages
-  // in flight.  BF16 pages fit twice: scores and P V of a page in the same
-  // iteration, one page in flight.
-  static constexpr bool PIPE = CACHE == kFp8;
-  static constexpr int NBUF = PIPE ? 4 : 2;
-  static constexpr int DIST = PIPE ? 2 : 1;          // pages in flight ahead of the current one
-  static constexpr int LOADS = PAGE_BYTES / 4096;  // 16-byte LDS-DMA loads per wave per page
-  static constexpr int PART = LOADS / 3;           // loads issued at each of three points
-  static constexpr int PSTRIDE = kPage * 2 + 16;   // bytes per P row in LDS
-  static constexpr int KBATCH = 9;                 // BF16 K reads issued before their math
-};
-
-// LDS layout of a staged BF16 page: token t's 16-byte chunk c (of NCH = 72 per
-// row) sits in chunk slot t * NCH + slot(t, c), the row rotated by 3 * (t / 2)
-// chunks, so that the 16-token operand reads of QK^T and the 8-token
-// transposed reads of PV hit distinct LDS banks.  The HBM -> LDS copy applies
-// the inverse mapping when it picks each lane's source chunk.  (FP8 pages use
-// their own grouped layout, defined with their kernel.)
-struct SwzBf16 {
-  static constexpr int NCH = 72;
-  __device__ static __forceinline__ int rot(int t) {  // in [0, NCH)
-    const int r = 3 * (t >> 1);
-    return r >= NCH ? r - NCH : r;  // t < 64 keeps r < 2 * NCH
-  }
-  __device__ static __forceinline__ int slot(int t, int c) {
-    const int v = c + rot(t);
-    return v >= NCH ? v - NCH : v;
-  }
-  __device__ static __forceinline__ int chunk_of_slot(int t, int s) {
-    const int v = s - rot(t);
-    return v < 0 ? v + NCH : v;
-  }
-};
 
 // Workgroup -> (request, split, row group) through decode_item (launch.h).
 // Grid size: decode_grid_size(B, max_splits, n_rg).

@@ -7,7 +7,7 @@
 
 namespace mla {
 int decode_rows_fp8() { return 64; }
-int decode_rows_per_group(int cache_kind) { return cache_kind == kFp8 ? 64 : 32; }
+int decode_rows_per_group(int cache_kind) { return cache_kind == kFp8 ? 64 : 64; }
 hipError_t launch_kv_append(const AppendArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_decode(const DecodeArgs&, int, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_decode_fp8(const DecodeArgs&, int, hipStream_t) { return hipErrorInvalidValue; }

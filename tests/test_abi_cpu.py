@@ -215,7 +215,7 @@ def test_noalloc_decode_validation(lib):
 
 
 # query rows per decode workgroup: 64 on an FP8 cache, 32 on a BF16 cache
-ROWS = {"fp8": 64, "bf16": 32}
+ROWS = {"fp8": 64, "bf16": 64}
 
 
 @pytest.mark.parametrize("dtype", ["fp8", "bf16"])
