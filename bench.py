@@ -510,7 +510,8 @@ def main():
         "ms_per_step_graph": None if ms_step_graph is None else round(ms_step_graph, 5),
         "append": ("none (the step's rows are already in the cache)" if w.n_new == 0
                    else "separate kv_append_fp8 launch" if args.separate_append
-                   else "in the decode launch (mla_decode_paged_append)"),
+                   else "in the decode launch (mla_decode_paged_append)" if w.n_new <= 16
+                   else "mla_decode_paged_append: its own kv_append launch first (more than 16 rows)"),
         "ms_per_step_eager": round(ms_step_eager, 5),
         "setup_s": round(t_setup, 1),
     }

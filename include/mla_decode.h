@@ -157,9 +157,8 @@ int kv_append_fp8(const void* kv_new, void* kv_cache, float* kv_scale, int scale
  * mla_decode_combine must run next; out and lse may then be NULL.
  * Supported: 1 <= H <= 128, 1 <= n_q <= 2048: a decode step's few new
  * tokens, or an extend / prefill chunk of up to 2048 new tokens, causal among
- * themselves, over the cached context (each group of 64 query rows on an FP8
- * cache, 32 on a BF16 cache, is a workgroup of its own that reads the pages of
- * its split).  A row that sees no token gets out = 0 and lse = -inf.
+ * themselves, over the cached context (each group of 64 query rows is a
+ * workgroup of its own that reads the pages of its split).  A row that sees no token gets out = 0 and lse = -inf.
  */
 int mla_decode_paged(const void* q, const void* kv_cache, int cache_dtype, const float* kv_scale,
                      int scale_mode, const int32_t* block_table, const int32_t* seq_lens, int B,
@@ -189,7 +188,13 @@ int mla_decode_paged(const void* q, const void* kv_cache, int cache_dtype, const
  * (seq_lens[b] - n_new + j < 0) is skipped, as in kv_append_fp8.  Errors as in
  * the two calls it replaces; MLA_ERR_UNSUPPORTED for MLA_SCALE_NONE.
  *
- *   store_rows      1: as above.  0: the new rows take part in this launch's
+ *   store_rows      1: as above.  With more than 16 new rows per request the
+ *                   rows are encoded and stored by a kv_append_fp8 launch on
+ *                   the same stream, and the decode launch that follows reads
+ *                   them back from the cache: every workgroup of the fused
+ *                   launch would otherwise encode them all again.  Same
+ *                   results; all arguments are checked before either launch.
+ *                   0: the new rows take part in this launch's
  *                   attention but nothing is written to kv_cache / kv_scale;
  *                   the caller stores them with kv_append_fp8 (for instance on
  *                   another stream, after kv_check_pages, with the checked

@@ -158,6 +158,54 @@ def test_fused_append_equals_separate(mode):
         compare(ob, lb, ref_o, ref_l, tag=f"fused {tag}")
 
 
+@pytest.mark.parametrize("mode", ["token", "tensor"])
+def test_long_append_paths_agree(mode):
+    """An append of 40 rows per request (an extend chunk): mla_decode_paged_append
+    storing the rows (they then go through their own append launch), the same
+    call with store_rows=0 (the rows encoded inside the decode launch) followed
+    by kv_append_fp8, and kv_append_fp8 + mla_decode_paged give the same cache,
+    scales, outputs and LSEs, bit for bit, and pass the oracle's bar; the new
+    rows straddle page boundaries and fill a request's first page."""
+    import long_context_mla_amd as mla
+
+    w = synth.custom(f"long_append_{mode}", B=3, n_q=40, H=16, context_lens=(30, 700, 0), cache_dtype="fp8",
+                     scale_mode=mode, append=40, seed=37)
+    log(f"long append {mode}: L={w.seq_lens.tolist()}")
+    ref_o, ref_l = oracle_decode(w)
+    max_pages = int(-(-w.seq_lens.max() // 64))
+    for pps, ms in [(max_pages, 1), (1, max_pages)]:
+        outs = []
+        for path in ("separate", "stored", "unstored"):
+            g = GpuState(w)
+            o = torch.empty((w.B, w.n_q, w.H, 512), dtype=torch.bfloat16, device=g.device)
+            l = torch.empty((w.B, w.n_q, w.H), dtype=torch.float32, device=g.device)
+            kw = dict(out=o, lse=l)
+            if ms > 1:
+                kw = dict(o_partial=torch.empty((w.B, ms, w.n_q, w.H, 512), dtype=torch.bfloat16, device=g.device),
+                          lse_partial=torch.empty((w.B, ms, w.n_q, w.H), dtype=torch.float32, device=g.device))
+            if path == "separate":
+                mla.kv_append_fp8(g.new_rows, g.cache, g.kv_scale, mode, g.block_table, g.seq_lens)
+                mla.mla_decode_paged(g.q, g.cache, g.kv_scale, mode, g.block_table, g.seq_lens, w.softmax_scale,
+                                     pps, ms, **kw)
+            else:
+                mla.mla_decode_paged_append(g.new_rows, g.q, g.cache, g.kv_scale, mode, g.block_table, g.seq_lens,
+                                            w.softmax_scale, pps, ms, store_rows=(path == "stored"), **kw)
+                if path == "unstored":
+                    mla.kv_append_fp8(g.new_rows, g.cache, g.kv_scale, mode, g.block_table, g.seq_lens)
+            if ms > 1:
+                mla.mla_decode_combine(kw["o_partial"], kw["lse_partial"], g.seq_lens, w.max_blocks, pps, o, l)
+            torch.cuda.synchronize()
+            outs.append((bf16_tensor_to_f64(o), l.cpu().double().numpy(), g.cache.cpu().numpy(),
+                         g.kv_scale.cpu().numpy()))
+        oa, la, ca, sa = outs[0]
+        for path, (ob, lb, cb, sb) in zip(("stored", "unstored"), outs[1:]):
+            tag = f"{mode} {path} pps={pps} splits={ms}"
+            assert np.array_equal(ca, cb), f"{tag}: cache differs at {np.argwhere(ca != cb)[:5]}"
+            assert np.array_equal(sa, sb), f"{tag}: scales differ"
+            assert np.array_equal(oa, ob) and np.array_equal(la, lb), f"{tag}: outputs differ"
+        compare(oa, la, ref_o, ref_l, tag=f"long append {mode} pps={pps} splits={ms}")
+
+
 def test_one_visible_token_returns_its_value():
     """L = 1: the only weight is 1, so out is the (dequantised) row itself."""
     for dtype, mode in (("fp8", "tensor"), ("fp8", "token"), ("bf16", "none")):
