@@ -67,10 +67,14 @@ struct CombineArgs {
   int B, R, max_blocks, pps, max_splits;
 };
 
-// Rows of the query matrix one decode workgroup owns: 64 on an FP8 cache
-// (decode_rows_fp8), 32 on a BF16 cache.
+// Rows of the query matrix one decode workgroup owns: 64 on either cache.
 int decode_rows_per_group(int cache_kind);
 int decode_rows_fp8();
+
+// Compute units of the part (256 in 8 XCDs).  A decode workgroup takes most of
+// a CU's LDS, so workgroups 0 .. kCUs-1 of a launch are the ones that start
+// together at its beginning.
+constexpr int kCUs = 256;
 
 // Workgroups of a decode launch (a 1-D grid): the B * max_splits work units
 // (request, split) padded to a multiple of the 8 XCDs, n_rg row groups each.

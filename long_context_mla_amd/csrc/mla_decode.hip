@@ -141,14 +141,11 @@ __global__ __launch_bounds__(512, 1) void decode_bf16_kernel(DecodeArgs a) {
   // is known (bounded by the table row), one per lane.
   int ids = 0;
   const int rh = wave & 1, th = (wave >> 1) & 1;
-  if (!scorer) {
-    const int32_t* id_src = a.block_table + bt_row + min(p_begin + lane, a.max_blocks - 1);
-    asm volatile("global_load_dword %0, %1, off" : "=v"(ids) : "v"(id_src) : "memory");
-  } else {
-    // The score waves copy the query of the group's 64 rows HBM -> LDS in 72
-    // coalesced 1 KB LDS-DMA copies (the rows are contiguous in q): slot s
-    // (16 bytes) of the staged query is row s / 72, chunk (s % 72) ^ ((row / 2) % 8).
-    // Rows past R repeat row R - 1.
+  // The score waves copy the query of the group's 64 rows HBM -> LDS in 72
+  // coalesced 1 KB LDS-DMA copies (the rows are contiguous in q): slot s
+  // (16 bytes) of the staged query is row s / 72, chunk (s % 72) ^ ((row / 2) % 8).
+  // Rows past R repeat row R - 1.
+  auto copy_query = [&]() {
     const uint8_t* qbase = reinterpret_cast<const uint8_t*>(a.q + (int64_t)b * a.R * kD);
 #pragma unroll
     for (int k = 0; k < kQLoads; ++k) {
@@ -159,7 +156,22 @@ __global__ __launch_bounds__(512, 1) void decode_bf16_kernel(DecodeArgs a) {
       const uint32_t dst = lds_addr(lds + (ii < 63 ? kQA + ii * 1024 : kQB + (ii - 63) * 1024));
       lds_dma16(qbase, (uint32_t)(min(r0 + r, a.R - 1) * kQRowBytes + c * 16), dst);
     }
+  };
+  const bool q_early = blockIdx.x < kCUs;
+  if (!scorer) {
+    const int32_t* id_src = a.block_table + bt_row + min(p_begin + lane, a.max_blocks - 1);
+    asm volatile("global_load_dword %0, %1, off" : "=v"(ids) : "v"(id_src) : "memory");
   }
+  // The launch's first round of workgroups (one per CU) issues the query
+  // copies before the length is known, so that their latency overlaps the
+  // length's (the test takes the whole table row as the length).  Later
+  // workgroups wait for the length and skip the copies for a split past the
+  // request's end: in a batch of mixed lengths most workgroups of the longest
+  // request's split count have no pages, and their query copies, spread over
+  // the launch, mostly missed in L2 (a 64-request pool read 986 MB per launch
+  // with them, 851 MB without).
+  const int L_test = q_early ? cap : min(max(load_const(a.seq_lens, b), 0), cap);
+  if (scorer && p_begin < (L_test + kPage - 1) / kPage) copy_query();
   const int L = min(max(load_const(a.seq_lens, b), 0), cap);
   const int n_pages = (L + kPage - 1) / kPage;
 
