@@ -6,11 +6,12 @@
 // One workgroup per (request, row, 128-dim chunk), 256 threads: 16 groups of
 // 16 lanes, each lane one 16-byte piece (8 values) of the chunk.  Up to 512
 // splits (the instantiation the launch picks) every lane loads all of its
-// group's partials (splits g, g + 16, ...)
-// at once, together with the split LSEs, before anything depends on them: one
-// memory round trip.  The split weights exp(lse_s - max_s lse_s) go through
-// LDS, each lane sums its splits from registers, and an LDS reduction folds
-// the 16 groups.  More splits than that stream through in blocks.
+// group's partials (splits g, g + 16, ...) at once, together with the split
+// LSEs, before anything depends on them: one memory round trip.  The split
+// weights exp(lse_s - max_s lse_s) go through LDS, each lane sums its splits
+// from registers; the four groups of a wave are folded on the VALU (permlane
+// swaps) and the four waves through LDS.  More splits than that stream
+// through in blocks.
 #include "device_common.h"
 #include "launch.h"
 
@@ -27,37 +28,86 @@ __device__ __forceinline__ void fma_bf16x8(f32x4 (&acc)[2], float w, u32x4 v) {
                       float_of(v.w & 0xffff0000u)};
 }
 
+// Maximum over the 16 lanes of each row (DPP rotations within the row), then
+// over the wave's four rows (permlane swaps), then over the four waves (LDS).
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  return fmaxf(v, float_of((uint32_t)__builtin_amdgcn_update_dpp(0, (int)bits_of(v), CTRL, 0xf, 0xf, false)));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  // row_ror:8, 4, 2, 1
+  return dpp_max<0x121>(dpp_max<0x122>(dpp_max<0x124>(dpp_max<0x128>(v))));
+}
+
 __device__ __forceinline__ float block_max(float v, float* s_red) {
-  v = wave_max(v);
+  v = group4_max(row16_max(v));
   if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
   __syncthreads();
   return fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
 }
 
-// The merge when the n_b splits fit NK loads per lane (16 * NK >= n_b >= 1):
-// group g loads splits g + 16k (the ones past n_b repeat split n_b - 1, a
-// written partial, and take weight 0).  ls0 / ls1 are this thread's split LSEs
-// (splits t and t + 256), already -inf past n_b.
+// Splits of request b that hold a partial: those that start before its last
+// page.  A request the page check flagged merges none: its rows come out
+// 0 / -inf.
+__device__ __forceinline__ int request_splits(const CombineArgs& a, int b) {
+  const int L = min(max(a.seq_lens[b], 0), a.max_blocks * kPage);
+  const int n_pages = (L + kPage - 1) / kPage;
+  return (a.status && a.status[b]) ? 0 : min(a.max_splits, (n_pages + a.pps - 1) / a.pps);
+}
+
+// The merge when the request's n_b splits fit NK loads per lane
+// (16 * NK >= n_b >= 1): group g loads splits g + 16k (the ones past n_b
+// repeat split n_b - 1, a written partial, and are left out of the sums).
+// ls0 / ls1 are this thread's split LSEs (splits t and t + 256; -inf at or
+// past max_splits).  (Loading the partials before the request's length
+// arrives, which a single request would allow, was slower: the loads are
+// bound by the memory's rate, and the length then came back behind them.)
 template <int NK>
-__device__ __forceinline__ void merge_held(const uint16_t* o_b, int64_t o_stride, float ls0, float ls1,
-                                           int n_b, float* s_w, float* s_red, f32x4 (&acc)[2],
-                                           float& wsum, float& M) {
+__device__ __forceinline__ void merge_held(const uint16_t* o_b, int64_t o_stride, float ls0, float ls1, int n_b,
+                                           float* s_w, float* s_red, f32x4 (&acc)[2], float& wsum, float& M) {
   const int t = threadIdx.x;
   const int g = t >> 4;
   u32x4 o[NK];
 #pragma unroll
   for (int k = 0; k < NK; ++k)
     o[k] = *reinterpret_cast<const u32x4*>(o_b + min(g + kGroups * k, n_b - 1) * o_stride);
+  // masked only now, so that the partial loads above do not wait for the LSEs
+  if (t >= n_b) ls0 = -INFINITY;
+  if (t + 256 >= n_b) ls1 = -INFINITY;
   M = block_max(fmaxf(ls0, ls1), s_red);
   s_w[t] = ls0 == -INFINITY ? 0.0f : expf(ls0 - M);
   if (NK * kGroups > 256) s_w[t + 256] = ls1 == -INFINITY ? 0.0f : expf(ls1 - M);
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < NK; ++k) {
-    const float w = g + kGroups * k < n_b ? s_w[g + kGroups * k] : 0.0f;
-    fma_bf16x8(acc, w, o[k]);
-    wsum += w;
+    if (g + kGroups * k < n_b) {
+      const float w = s_w[g + kGroups * k];
+      fma_bf16x8(acc, w, o[k]);
+      wsum += w;
+    }
   }
+}
+
+// ceil(n_b / 16) loads per lane rounded up to a power of two, so that each
+// count is straight-line code with every load in flight at once (n_b is
+// uniform over the workgroup; an empty request merges nothing).
+template <int MAXK>
+__device__ __forceinline__ void merge_held_any(const uint16_t* o_b, int64_t o_stride, float ls0, float ls1,
+                                               int n_b, float* s_w, float* s_red, f32x4 (&acc)[2], float& wsum,
+                                               float& M) {
+  const int n_k = (n_b + kGroups - 1) / kGroups;
+  if (MAXK >= 32 && n_k > 16)
+    merge_held<(MAXK >= 32 ? 32 : 1)>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
+  else if (MAXK >= 16 && n_k > 8)
+    merge_held<(MAXK >= 16 ? 16 : 1)>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
+  else if (MAXK >= 8 && n_k > 4)
+    merge_held<(MAXK >= 8 ? 8 : 1)>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
+  else if (n_k > 2)
+    merge_held<4>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
+  else if (n_k > 1)
+    merge_held<2>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
+  else if (n_k == 1)
+    merge_held<1>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
 }
 
 // MAXK: the most partial loads a lane holds at once (splits up to 16 * MAXK
@@ -75,48 +125,26 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int g = t >> 4;  // split group
   __shared__ float s_w[kWeightChunk];
   __shared__ float s_red[4];
-  __shared__ f32x4 s_acc[kGroups][16][2];
-  __shared__ float s_ws[kGroups];
+  __shared__ f32x4 s_acc[4][16][2];
+  __shared__ float s_ws[4];
 
   const float* lse_b = a.lse_part + (int64_t)b * a.max_splits * a.R + r;
   const uint16_t* o_b = a.o_part + ((int64_t)b * a.max_splits * a.R + r) * kDV + chunk * 128 + c * 8;
   const int64_t o_stride = (int64_t)a.R * kDV;
-  // Up to kHeldSplits splits (the usual case) the split LSEs are loaded
-  // before the length is known: every entry below max_splits lies in the
-  // buffer, and the ones past the request's splits are masked once the length
-  // arrives.
+  // Up to 16 * MAXK splits (the usual case) the split LSEs are loaded before
+  // the length is known: every entry below max_splits lies in the buffer, and
+  // the ones past the request's splits are masked once the length arrives.
   const bool held = a.max_splits <= kGroups * MAXK;
   float ls0 = -INFINITY, ls1 = -INFINITY;
   if (held && t < a.max_splits) ls0 = lse_b[(int64_t)t * a.R];
   if (held && t + 256 < a.max_splits) ls1 = lse_b[(int64_t)(t + 256) * a.R];
 
-  const int L = min(max(a.seq_lens[b], 0), a.max_blocks * kPage);
-  const int n_pages = (L + kPage - 1) / kPage;
-  // a request the page check flagged merges no split: its rows come out 0 / -inf
-  const int n_b = (a.status && a.status[b]) ? 0 : min(a.max_splits, (n_pages + a.pps - 1) / a.pps);
-
   f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   float wsum = 0.0f;
   float M = -INFINITY;
+  const int n_b = request_splits(a, b);
   if (held) {
-    // ceil(n_b / 16) loads per lane, rounded up to a power of two so that each
-    // count is straight-line code with every load in flight at once (the
-    // count is uniform over the workgroup).  An empty request merges nothing.
-    if (t >= n_b) ls0 = -INFINITY;
-    if (t + 256 >= n_b) ls1 = -INFINITY;
-    const int n_k = (n_b + kGroups - 1) / kGroups;
-    if (MAXK >= 32 && n_k > 16)
-      merge_held<(MAXK >= 32 ? 32 : 1)>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
-    else if (MAXK >= 16 && n_k > 8)
-      merge_held<(MAXK >= 16 ? 16 : 1)>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
-    else if (MAXK >= 8 && n_k > 4)
-      merge_held<(MAXK >= 8 ? 8 : 1)>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
-    else if (n_k > 2)
-      merge_held<4>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
-    else if (n_k > 1)
-      merge_held<2>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
-    else if (n_k == 1)
-      merge_held<1>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
+    merge_held_any<MAXK>(o_b, o_stride, ls0, ls1, n_b, s_w, s_red, acc, wsum, M);
   } else {
     float m = -INFINITY;
     for (int s = t; s < n_b; s += 256) m = fmaxf(m, lse_b[(int64_t)s * a.R]);
@@ -148,15 +176,25 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       }
     }
   }
-  s_acc[g][c][0] = acc[0];
-  s_acc[g][c][1] = acc[1];
-  if (c == 0) s_ws[g] = wsum;
+  // fold the wave's four split groups on the VALU, then the four waves through LDS
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[0][i] = group4_sum(acc[0][i]);
+    acc[1][i] = group4_sum(acc[1][i]);
+  }
+  wsum = group4_sum(wsum);
+  const int wv = t >> 6;
+  if ((t & 63) < 16) {
+    s_acc[wv][c][0] = acc[0];
+    s_acc[wv][c][1] = acc[1];
+    if (c == 0) s_ws[wv] = wsum;
+  }
   __syncthreads();
-  if (g == 0) {
+  if (t < 16) {
     f32x4 lo = s_acc[0][c][0], hi = s_acc[0][c][1];
     float wt = s_ws[0];
 #pragma unroll
-    for (int k = 1; k < kGroups; ++k) {
+    for (int k = 1; k < 4; ++k) {
       lo += s_acc[k][c][0];
       hi += s_acc[k][c][1];
       wt += s_ws[k];
