@@ -50,9 +50,13 @@ __device__ __forceinline__ float block_max(float v, float* s_red) {
 // page.  A request the page check flagged merges none: its rows come out
 // 0 / -inf.
 __device__ __forceinline__ int request_splits(const CombineArgs& a, int b) {
-  const int L = min(max(a.seq_lens[b], 0), a.max_blocks * kPage);
+  // both loads go out together (without a status the length is read twice)
+  const int st = (a.status ? a.status : a.seq_lens)[b];
+  const int raw = a.seq_lens[b];
+  asm volatile("" :: "s"(st), "s"(raw));
+  const int L = min(max(raw, 0), a.max_blocks * kPage);
   const int n_pages = (L + kPage - 1) / kPage;
-  return (a.status && a.status[b]) ? 0 : min(a.max_splits, (n_pages + a.pps - 1) / a.pps);
+  return (a.status && st != 0) ? 0 : min(a.max_splits, (n_pages + a.pps - 1) / a.pps);
 }
 
 // The merge when the request's n_b splits fit NK loads per lane
@@ -211,7 +215,83 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   }
 }
 
+// The merge for a batch of many rows over few splits (max_splits <= 64): one
+// wave per row of the query matrix (request b, row r), lane l holding dims
+// 8l .. 8l+7 of the 512, so that a split's partial row is one coalesced 1 KB
+// load and the wave needs no LDS and no barrier.  Lane s holds split s's LSE;
+// the partial loads go out kRowChunk splits at a time, each chunk's loads
+// before the previous chunk is summed.  (The workgroup-per-row-chunk form
+// above spreads one row's splits over 16 groups: for a batch of short merges
+// most of its lanes idle and every workgroup is one dependent chain of loads.)
+constexpr int kRowChunk = 8;
+constexpr int kRowMaxSplits = 64;
+constexpr int kRowsPerGroup = 4;  // waves (rows) per 256-thread workgroup
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += float_of((uint32_t)__builtin_amdgcn_update_dpp(0, (int)bits_of(v), 0x128, 0xf, 0xf, false));
+  v += float_of((uint32_t)__builtin_amdgcn_update_dpp(0, (int)bits_of(v), 0x124, 0xf, 0xf, false));
+  v += float_of((uint32_t)__builtin_amdgcn_update_dpp(0, (int)bits_of(v), 0x122, 0xf, 0xf, false));
+  v += float_of((uint32_t)__builtin_amdgcn_update_dpp(0, (int)bits_of(v), 0x121, 0xf, 0xf, false));
+  return v;
+}
+
+__global__ __launch_bounds__(256) void combine_rows_kernel(CombineArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar loads below
+  const int64_t br = (int64_t)blockIdx.x * kRowsPerGroup + wv;  // b * R + r
+  if (br >= (int64_t)a.B * a.R) return;
+  const int b = (int)(br / a.R);
+  const int r = (int)(br - (int64_t)b * a.R);
+  const int64_t row0 = (int64_t)b * a.max_splits * a.R + r;  // (b, split 0, r)
+  // the split LSEs go out before the length is known (every entry below
+  // max_splits lies in the buffer); those past the request's splits are
+  // masked once it arrives
+  float ls = lane < a.max_splits ? a.lse_part[row0 + (int64_t)lane * a.R] : -INFINITY;
+  const int n_b = request_splits(a, b);
+  const uint16_t* src = a.o_part + row0 * kDV + 8 * lane;
+  const int64_t stride = (int64_t)a.R * kDV;  // between the splits of one row
+  const int nch = (n_b + kRowChunk - 1) / kRowChunk;
+  u32x4 o[2][kRowChunk];
+  auto load_chunk = [&](int c, u32x4 (&d)[kRowChunk]) {
+#pragma unroll
+    for (int k = 0; k < kRowChunk; ++k)
+      d[k] = *reinterpret_cast<const u32x4*>(src + min(kRowChunk * c + k, n_b - 1) * stride);
+  };
+  if (nch > 0) load_chunk(0, o[0]);
+  if (lane >= n_b) ls = -INFINITY;
+  const float M = group4_max(row16_max(ls));
+  const float w = ls == -INFINITY ? 0.0f : expf(ls - M);
+  const float wsum = group4_sum(row16_sum(w));
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int c = 0; c < kRowMaxSplits / kRowChunk; ++c) {
+    if (c < nch) {
+      if (c + 1 < nch) load_chunk(c + 1, o[(c + 1) & 1]);
+#pragma unroll
+      for (int k = 0; k < kRowChunk; ++k) {
+        const int sp = kRowChunk * c + k;
+        if (sp < n_b) fma_bf16x8(acc, float_of(__builtin_amdgcn_readlane(bits_of(w), sp)), o[c & 1][k]);
+      }
+    }
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  u32x4 v;
+  v.x = float_to_bf16(acc[0][0] * inv) | (uint32_t(float_to_bf16(acc[0][1] * inv)) << 16);
+  v.y = float_to_bf16(acc[0][2] * inv) | (uint32_t(float_to_bf16(acc[0][3] * inv)) << 16);
+  v.z = float_to_bf16(acc[1][0] * inv) | (uint32_t(float_to_bf16(acc[1][1] * inv)) << 16);
+  v.w = float_to_bf16(acc[1][2] * inv) | (uint32_t(float_to_bf16(acc[1][3] * inv)) << 16);
+  *reinterpret_cast<u32x4*>(a.out + br * kDV + 8 * lane) = v;
+  if (lane == 0) a.lse[br] = wsum > 0.0f ? M + logf(wsum) : -INFINITY;
+}
+
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.B * a.R;
+  if (a.max_splits <= kRowMaxSplits && rows >= 1024) {
+    // many rows over few splits: a wave per row (at least 256 workgroups)
+    const dim3 grid((unsigned)((rows + kRowsPerGroup - 1) / kRowsPerGroup)), block(256);
+    hipLaunchKernelGGL(combine_rows_kernel, grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
   const dim3 grid(a.B * a.R * 4), block(256);
   if (a.max_splits <= kGroups * 4)
     hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, stream, a);
