@@ -390,3 +390,49 @@ def test_rows_without_a_slot_are_not_stored(path):
     ref_o, ref_l = oracle_decode(w, requests=[2])
     compare(bf16_tensor_to_f64(out), lse.detach().cpu().double().numpy(), ref_o, ref_l, requests=[2],
             tag=f"no-slot {name}")
+
+
+@pytest.mark.parametrize("check_mode", ["front", "launch"])
+def test_flagged_request_in_a_wide_batch(check_mode):
+    """A batch of 1,024 query rows over at most 64 splits (the combine then
+    merges a row per wave): the flagged request's rows come out 0 / -inf, the
+    cache is as the oracle's check-and-append leaves it, the others match the
+    attention oracle."""
+    lens = (63, 64, 65, 700, 1500, 2999, 1, 128, 5, 900, 2000, 1280, 333, 3999, 17, 0)
+    w = synth.custom("wide_check", B=16, n_q=1, H=64, context_lens=lens, cache_dtype="fp8", scale_mode="token",
+                     seed=41)
+    rng = np.random.default_rng(43)
+    tags = rng.integers(0, 2**32, size=w.num_pages, dtype=np.uint64).astype(np.uint32)
+    bt = w.block_table
+    et = np.where(bt >= 0, tags[np.clip(bt, 0, w.num_pages - 1)], 0).astype(np.uint32)
+    victim = 4
+    tags[int(bt[victim, 3])] ^= np.uint32(1)  # an earlier page of the victim was handed out again
+    want_s, want_l = oi.check_pages_ref(tags, bt, et, w.seq_lens)
+    assert [i for i, s in enumerate(want_s) if s] == [victim]
+    import long_context_mla_amd as mla
+
+    for pps in (1, 2):
+        npg = int(-(-w.seq_lens.max() // 64))
+        ms = -(-npg // pps)
+        assert ms <= 64 and w.B * w.n_q * w.H >= 1024
+        log(f"wide check {check_mode} pps={pps} splits={ms} rows={w.B * w.n_q * w.H}")
+        g = GpuState(w)
+        st = mla.DecodeStep(w.B, w.n_q, w.H, w.max_blocks, int(w.seq_lens.max()), w.total_tokens(), g.device,
+                            pages_per_split=pps, max_splits=ms, fuse_append=True, check_mode=check_mode,
+                            cache_dtype=w.cache_dtype)
+        out, lse = st(g.q, g.cache, g.kv_scale, g.scale_mode, g.block_table, g.seq_lens, w.softmax_scale,
+                      new_rows=g.new_rows, page_check=(_dev(tags), _dev(et), None))
+        torch.cuda.synchronize()
+        assert st.status.cpu().numpy().tolist() == want_s.tolist()
+        o = bf16_tensor_to_f64(out)
+        l = lse.detach().cpu().double().numpy()
+        assert not o[victim].any() and np.all(np.isneginf(l[victim]))
+        cache, scales, ts = oracle_pool(w)
+        if check_mode == "launch":
+            oi.append_checked_ref(w.new_row_bits(), cache, scales, bt, w.seq_lens, w.scale_mode, ts, tags, et)
+        else:
+            omla.append_ref(w.new_row_bits(), cache, scales, bt, want_l, w.scale_mode, ts)
+        assert_cache_equals(g, cache, scales, f"wide check {check_mode} pps={pps}")
+        keep = [b for b in range(w.B) if b != victim]
+        ref_o, ref_l = oracle_decode(w, requests=keep)
+        compare(o, l, ref_o, ref_l, requests=keep, tag=f"wide check {check_mode} pps={pps}")
