@@ -32,8 +32,8 @@ CASES = [
          scale_mode="token"),
     dict(name="fp8_empty_req", B=2, n_q=1, H=64, context_lens=(0, 100), cache_dtype="fp8",
          scale_mode="token", append=0),
-    # the header's limits: H up to 128, n_q up to 8 (up to 16 row groups of 64 on FP8,
-    # 32 of 32 on BF16), full and ragged last pages
+    # H up to 128 and n_q up to 8 (up to 16 row groups of 64 query rows), full and
+    # ragged last pages
     dict(name="fp8_h128", B=2, n_q=1, H=128, context_lens=(2000, 63), cache_dtype="fp8", scale_mode="token"),
     dict(name="fp8_nq5_h64", B=2, n_q=5, H=64, context_lens=(1019, 3), cache_dtype="fp8", scale_mode="token"),
     dict(name="fp8_nq8_h128", B=1, n_q=8, H=128, context_lens=(632,), cache_dtype="fp8", scale_mode="tensor"),
@@ -282,8 +282,8 @@ def test_page_permutation_and_determinism_bitwise():
 def test_fp8_equals_bf16_on_the_e4m3_grid():
     """Cache values exactly representable in e4m3 with scale 1: the FP8 path and
     the BF16 path see identical numbers.  The two kernels feed the tokens to the
-    matrix core in different orders (64 and 32 query rows per workgroup, other
-    k orders), so fp32 rounding may differ; a wrong decode of any code would
+    matrix core in different orders (pages against half-page units, other k
+    orders), so fp32 rounding may differ; a wrong decode of any code would
     not stay inside these bounds (the codes span the whole e4m3 range, so the
     softmax is peaked and each output row is dominated by a few decoded rows)."""
     w8 = synth.custom("grid", B=2, n_q=2, H=64, context_lens=(900, 130), cache_dtype="fp8",
