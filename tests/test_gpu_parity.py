@@ -45,6 +45,11 @@ CASES = [
     dict(name="bf16_extend_nq64", B=2, n_q=64, H=16, context_lens=(300, 1000), cache_dtype="bf16"),
     dict(name="fp8_extend_nq130", B=1, n_q=130, H=16, context_lens=(700,), cache_dtype="fp8",
          scale_mode="token"),
+    # the largest chunk the header allows: 2048 new tokens (32 and 64 row groups), whose
+    # append on the FP8 cache takes its own launch
+    dict(name="fp8_extend_nq2048", B=1, n_q=2048, H=1, context_lens=(150,), cache_dtype="fp8",
+         scale_mode="token"),
+    dict(name="bf16_extend_nq2048_h2", B=1, n_q=2048, H=2, context_lens=(2200,), cache_dtype="bf16"),
 ]
 
 
