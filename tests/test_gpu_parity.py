@@ -429,3 +429,39 @@ def test_five_score_jumps_in_one_split(cache_dtype):
     for pps, ms in [(npg, 1), (16, 2)]:
         o, l = g.decode_only(pps, ms)
         compare(o, l, ref_o, ref_l, tag=f"five jumps {cache_dtype} pps={pps} splits={ms}")
+
+
+def _random_case(rng, i):
+    """A seeded random configuration: batch, query tokens, heads, lengths (page
+    boundaries, empty requests and sub-page tails included), cache kind, scale
+    mode, appended rows and split plan."""
+    dtype = ["fp8", "fp8", "bf16"][i % 3]
+    B = int(rng.integers(1, 7))
+    n_q = int(rng.choice([1, 1, 2, 3, 4, 7, 16]))
+    H = int(rng.choice([1, 8, 16, 40, 64, 128]))
+    edge = [0, 1, 63, 64, 65, 127, 128, 129]
+    lens = tuple(int(rng.choice(edge)) if rng.random() < 0.35 else int(rng.integers(0, 3000)) for _ in range(B))
+    kw = dict(scale_mode=str(rng.choice(["tensor", "token"]))) if dtype == "fp8" else {}
+    if dtype == "fp8":
+        kw["append"] = int(rng.choice([0, n_q, n_q, 3]))
+    w = synth.custom(f"rand{i}", B=B, n_q=n_q, H=H, context_lens=lens, cache_dtype=dtype, seed=100 + i,
+                     extra_blocks=int(rng.integers(0, 3)), **kw)
+    max_pages = max(int(-(-int(w.seq_lens.max()) // 64)), 1)
+    pps = int(rng.integers(1, max_pages + 1))
+    return w, pps, -(-max_pages // pps)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_configurations(i):
+    """Seeded random shapes against the oracle, with the planner's split plan
+    and with a random one (the append stored in the first step)."""
+    rng = np.random.default_rng(2024 + i)
+    w, pps, ms = _random_case(rng, i)
+    log(f"random {i}: {w.cache_dtype} {w.scale_mode} B={w.B} n_q={w.n_q} H={w.H} n_new={w.n_new} "
+        f"L={w.seq_lens.tolist()} plan={pps}x{ms}")
+    g = GpuState(w)
+    ref_o, ref_l = oracle_decode(w)
+    out, lse = g.step()
+    compare(out, lse, ref_o, ref_l, tag=f"random {i} planned")
+    o, l = g.decode_only(pps, ms)
+    compare(o, l, ref_o, ref_l, tag=f"random {i} pps={pps} splits={ms}")
