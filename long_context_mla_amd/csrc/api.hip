@@ -389,9 +389,10 @@ int mla_decode_plan_lens(const int32_t* seq_lens, int B, int n_q, int H, int num
   // order); it waits there for the first of its num_cus / 8 compute units to
   // come free (one workgroup per unit at a time) and costs its pages plus a
   // small fixed start and end.  Workgroups past a request's last page exit at
-  // once and are skipped.  (Fitted by measurement on MI355X: with this model
-  // the plan it ranks first was the fastest measured on every batched
-  // workload.)
+  // once and are skipped.  (Fitted by measurement on MI355X.  The model sees
+  // neither the L2 sharing of co-scheduled workgroups nor a page interval
+  // that shortens as fewer units copy at once: on the batched workloads its
+  // pick measured within 3-6 % of the fastest split length found by a sweep.)
   constexpr int64_t kFixedPages = 2;
   const int per_xcd = std::max(1, num_cus / 8);
   auto makespan = [&](int pps) {
