@@ -9,21 +9,9 @@ namespace mla {
 
 constexpr float kRefSlack = 64.0f;  // log2 headroom of the weights over the reference
 
-// Workgroup -> (request, split, row group) through decode_item (launch.h).
-// Grid size: decode_grid_size(B, max_splits, n_rg).
-struct WorkUnit {
-  int b, split, rg;
-  bool valid;
-};
+// This workgroup's (request, split, row group): work_unit_of (launch.h).
 __device__ __forceinline__ WorkUnit decode_work_unit(int B, int max_splits, int n_rg) {
-  const int v = (int)decode_item(blockIdx.x, B, max_splits, n_rg);
-  const int u = v / n_rg;
-  WorkUnit w;
-  w.rg = v - u * n_rg;
-  w.valid = u < B * max_splits;
-  w.split = w.valid ? u / B : 0;
-  w.b = w.valid ? u - w.split * B : 0;
-  return w;
+  return work_unit_of(blockIdx.x, B, max_splits, n_rg);
 }
 
 template <int N>

@@ -99,6 +99,24 @@ __host__ __device__ inline int64_t decode_item(int64_t i, int64_t B, int64_t max
   return (k << 6) | (((x - k) & 7) << 3) | t;
 }
 
+// Workgroup i of a decode launch -> (request b, split, row group rg) of item
+// decode_item(i); valid is false for the grid's padding past B * max_splits
+// units.  Shared by the kernels and the host-side tests of the map.
+struct WorkUnit {
+  int b, split, rg;
+  bool valid;
+};
+__host__ __device__ inline WorkUnit work_unit_of(int64_t i, int B, int max_splits, int n_rg) {
+  const int v = (int)decode_item(i, B, max_splits, n_rg);
+  const int u = v / n_rg;
+  WorkUnit w;
+  w.rg = v - u * n_rg;
+  w.valid = u < B * max_splits;
+  w.split = w.valid ? u / B : 0;
+  w.b = w.valid ? u - w.split * B : 0;
+  return w;
+}
+
 hipError_t launch_kv_append(const AppendArgs& a, int scale_mode, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int cache_kind, int scale_mode, hipStream_t stream);
 hipError_t launch_decode_fp8(const DecodeArgs& a, int scale_mode, hipStream_t stream);

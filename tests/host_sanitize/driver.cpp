@@ -6,10 +6,12 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <initializer_list>
 #include <random>
 #include <vector>
 
 #include "../../include/mla_decode.h"
+#include "../../long_context_mla_amd/csrc/launch.h"
 
 static int failures = 0;
 #define EXPECT(cond)                                                  \
@@ -73,6 +75,29 @@ int main() {
   int pps = 0, ms = 0;
   EXPECT(mla_decode_plan_lens(bad.data(), 2, 1, 64, 0, 1, &pps, &ms) == MLA_ERR_BAD_SHAPE);
   EXPECT(mla_decode_plan_lens(bad.data(), 2, 1, 64, 0, 9, &pps, &ms) == MLA_ERR_UNSUPPORTED);
+  // the kernels' workgroup -> work-unit map: every (request, split, row group)
+  // exactly once, every field in range, only padding invalid
+  for (int B : {1, 2, 3, 7, 16, 32, 64, 100}) {
+    for (int ms : {1, 2, 4, 9, 40, 224}) {
+      for (int n_rg : {1, 2, 4, 16}) {
+        const int64_t grid = mla::decode_grid_size(B, ms, n_rg);
+        std::vector<char> seen((size_t)B * ms * n_rg, 0);
+        int64_t n_valid = 0;
+        for (int64_t i = 0; i < grid; ++i) {
+          const mla::WorkUnit w = mla::work_unit_of(i, B, ms, n_rg);
+          if (!w.valid) continue;
+          ++n_valid;
+          const bool ok = w.b >= 0 && w.b < B && w.split >= 0 && w.split < ms && w.rg >= 0 && w.rg < n_rg;
+          EXPECT(ok);
+          if (!ok) continue;
+          char& s = seen[((size_t)w.split * B + w.b) * n_rg + w.rg];
+          EXPECT(s == 0);
+          s = 1;
+        }
+        EXPECT(n_valid == (int64_t)B * ms * n_rg);
+      }
+    }
+  }
   std::printf("host sanitizer driver: %d failures\n", failures);
   return failures ? 1 : 0;
 }

@@ -2,7 +2,9 @@
 (CPU only): api.hip (argument validation, the split planners, the item order
 they model, the status strings) is built for the host with both sanitizers,
 with stub kernel launchers, and driven by tests/host_sanitize/driver.cpp
-through every validation path and 400 random batches of the planners.  The
+through every validation path and 400 random batches of the planners; the
+driver also checks that the kernels' workgroup -> work-unit map covers every
+(request, split, row group) once, in range, for a grid of batch shapes.  The
 sanitizers instrument host code only; the device side is built as usual and
 never runs here."""
 
