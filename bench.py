@@ -3,8 +3,9 @@
 
 A step is the whole hot path on one batch: the step's new latent rows go into
 the FP8 cache and the split-KV decode runs in one launch
-(mla_decode_paged_append: kv_append_fp8 + mla_decode_paged), then
-mla_decode_combine (--separate-append issues kv_append_fp8 on its own).  Steps are
+(mla_decode_paged_append: kv_append_fp8 + mla_decode_paged; an extend chunk of
+more than 16 rows per request gets the append's own launch inside that call),
+then mla_decode_combine (--separate-append issues kv_append_fp8 on its own).  Steps are
 timed twice, launched eagerly and as replays of HIP graphs that each hold one
 step on every rotated cache in turn (a serving loop's form: a model's
 consecutive layers, each with its own cache, in one graph); the step time is
